@@ -1,0 +1,142 @@
+"""fp64 CPU oracle for sparse-MLA decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It wraps `oracle.c` (plain C, fp64, OpenMP) through ctypes and
+shares no code with the HIP library it checks.  What it computes, and the
+readings it takes where the pages are silent, are stated in `oracle.c`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+FMT_BF16 = 0
+FMT_FP8 = 1
+
+
+def build(out_path: str = _LIB_PATH, defines: tuple[str, ...] = ()) -> str:
+    """Compile oracle.c with gcc (-O2, IEEE semantics, OpenMP) into a shared library."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", *[f"-D{d}" for d in defines], _SRC, "-o", out_path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def _bind(lib):
+    c = ctypes
+    p = c.c_void_p
+    lib.oracle_e4m3_to_f64.restype = c.c_double
+    lib.oracle_e4m3_to_f64.argtypes = [c.c_uint8]
+    lib.oracle_bf16_to_f64.restype = c.c_double
+    lib.oracle_bf16_to_f64.argtypes = [c.c_uint16]
+    lib.oracle_row_bytes.restype = c.c_int
+    lib.oracle_row_bytes.argtypes = [c.c_int]
+    lib.oracle_decode_row.restype = None
+    lib.oracle_decode_row.argtypes = [c.c_int, p, p]
+    lib.oracle_gather.restype = c.c_int
+    lib.oracle_gather.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int64, c.c_int, p, p, p, p, p, p]
+    lib.oracle_decode.restype = c.c_int
+    lib.oracle_decode.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int64, c.c_int,
+                                  p, p, p, p, p, c.c_float, p, p, c.c_int]
+    lib.oracle_max_threads.restype = c.c_int
+    lib.oracle_max_threads.argtypes = []
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the built oracle (building it first if absent).  A path loads a variant."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def e4m3_to_f64(code: int, lib=None) -> float:
+    return (lib or load()).oracle_e4m3_to_f64(int(code))
+
+
+def bf16_to_f64(bits: int, lib=None) -> float:
+    return (lib or load()).oracle_bf16_to_f64(int(bits))
+
+
+def decode_row(kv_format: int, row: np.ndarray, lib=None) -> np.ndarray:
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    x = np.zeros(576, dtype=np.float64)
+    (lib or load()).oracle_decode_row(int(kv_format), _ptr(row), _ptr(x))
+    return x
+
+
+def gather(q_shape_B: int, topk: int, kv_format: int, kv_pool: np.ndarray, pool_pages: int,
+           page_table: np.ndarray, topk_idx: np.ndarray, ctx_len: np.ndarray,
+           with_rows: bool = True, lib=None):
+    """Index translation + row gather: (slots int64 [B, topk], rows uint8 [B, topk, row_bytes])."""
+    lib = lib or load()
+    B = int(q_shape_B)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    rb = lib.oracle_row_bytes(int(kv_format))
+    slots = np.empty((B, topk), dtype=np.int64)
+    rows = np.empty((B, topk, rb), dtype=np.uint8) if with_rows else None
+    rc = lib.oracle_gather(B, topk, pt.shape[1], int(pool_pages), int(kv_format), _ptr(kv_pool),
+                           _ptr(pt), _ptr(idx), _ptr(ctx), _ptr(slots),
+                           _ptr(rows) if with_rows else None)
+    if rc != 0:
+        raise ValueError(f"oracle_gather failed ({rc})")
+    return slots, rows
+
+
+def decode(q: np.ndarray, kv_format: int, kv_pool: np.ndarray, pool_pages: int,
+           page_table: np.ndarray, topk_idx: np.ndarray, ctx_len: np.ndarray, scale,
+           nthreads: int = 0, lib=None):
+    """Attention over the selected rows: (out float64 [B, H, 512], lse float64 [B, H])."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, H, dqk = q.shape
+    assert dqk == 576
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    out = np.zeros((B, H, 512), dtype=np.float64)
+    lse = np.zeros((B, H), dtype=np.float64)
+    rc = lib.oracle_decode(B, H, idx.shape[1], pt.shape[1], int(pool_pages), int(kv_format),
+                           _ptr(q), _ptr(kv_pool), _ptr(pt), _ptr(idx), _ptr(ctx),
+                           float(np.float32(scale)), _ptr(out), _ptr(lse), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed ({rc})")
+    return out, lse
+
+
+def decode_workload(w, nthreads: int = 0, lib=None, pool: np.ndarray | None = None):
+    """Convenience: run `decode` on a workloads.Workload."""
+    if pool is None:
+        pool = w.host_pool()
+    return decode(w.q, w.kv_format, pool, w.pool_pages, w.page_table, w.topk_idx, w.ctx_len,
+                  w.scale, nthreads=nthreads, lib=lib)
+
+
+def gather_workload(w, with_rows: bool = True, lib=None, pool: np.ndarray | None = None):
+    if pool is None:
+        pool = w.host_pool()
+    return gather(w.B, w.topk_idx.shape[1], w.kv_format, pool, w.pool_pages, w.page_table,
+                  w.topk_idx, w.ctx_len, with_rows=with_rows, lib=lib)
+
+
+def max_threads(lib=None) -> int:
+    return (lib or load()).oracle_max_threads()

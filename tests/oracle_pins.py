@@ -1,0 +1,336 @@
+"""Pins of the fp64 oracle against what the mathematics and library routines fix.
+
+Each `pin_*` takes a loaded oracle library (the real one, or a variant with a
+planted mistake) and raises AssertionError when the oracle disagrees.  Nothing
+here re-types the oracle's attention arithmetic: attention is checked against
+torch's scaled_dot_product_attention / logsumexp in float64, against closed
+forms and invariants, and against a pure-Python brute force on tiny inputs;
+element decoders are checked against torch's own fp8/bf16 casts.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+TOL = 1e-11
+
+
+# ----------------------------------------------------------------- test-side helpers
+def _torch_rows(fmt: int, rows: np.ndarray):
+    """(K float64 [n,576], V float64 [n,512]) from row bytes, decoded with torch casts."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    n = rows.shape[0]
+    if fmt == W.FMT_FP8:
+        codes = torch.from_numpy(rows[:, :512].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+        scales = torch.from_numpy(rows[:, 512:528].copy().view("<f4").astype(np.float64)).reshape(n, 4)
+        lat = codes * scales.repeat_interleave(128, dim=1)
+        rope = torch.from_numpy(rows[:, 528:656].copy().view("<u2").astype(np.int16)).view(torch.bfloat16)
+    else:
+        lat = torch.from_numpy(rows[:, :1024].copy().view("<u2").astype(np.int16)).view(torch.bfloat16)
+        lat = lat.to(torch.float64)
+        rope = torch.from_numpy(rows[:, 1024:1152].copy().view("<u2").astype(np.int16)).view(torch.bfloat16)
+    k = torch.cat([lat, rope.to(torch.float64)], dim=1)
+    return k, lat.clone()
+
+
+def _q64(w: W.Workload) -> torch.Tensor:
+    return torch.from_numpy(w.q.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+
+
+def _valid_rows(w: W.Workload, pool: np.ndarray, b: int) -> np.ndarray:
+    rb = w.row_bytes
+    out = []
+    for i in w.topk_idx[b]:
+        if 0 <= i < w.ctx_len[b]:
+            page = int(w.page_table[b, i // W.PAGE])
+            out.append(pool[(page * W.PAGE + i % W.PAGE) * rb:(page * W.PAGE + i % W.PAGE + 1) * rb])
+    return np.array(out, dtype=np.uint8).reshape(len(out), rb)
+
+
+def _context_rows(w: W.Workload, pool: np.ndarray, b: int) -> np.ndarray:
+    """Rows of tokens 0..ctx-1 of request b, in token order (dense context)."""
+    rb = w.row_bytes
+    out = []
+    for t in range(int(w.ctx_len[b])):
+        slot = int(w.page_table[b, t // W.PAGE]) * W.PAGE + t % W.PAGE
+        out.append(pool[slot * rb:(slot + 1) * rb])
+    return np.array(out, dtype=np.uint8).reshape(len(out), rb)
+
+
+def _dense_ws(fmt: int):
+    """Selections that cover the whole context: dense attention over every token."""
+    ctx = [512, 300, 1]
+    idx = np.full((3, W.TOPK), -1, np.int32)
+    rng = np.random.default_rng(11)
+    for b, c in enumerate(ctx):
+        idx[b, :c] = rng.permutation(c)
+    rng.shuffle(idx[1])           # masked slots scattered among valid ones
+    return W.build("dense", 901, fmt, 3, ctx, fmt, "given", topk_idx=idx)
+
+
+# ----------------------------------------------------------------- pins
+def pin_e4m3_all_codes(lib):
+    """All 256 e4m3fn codes decode as torch's float8_e4m3fn cast decodes them."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+    for c in range(256):
+        got = oracle.e4m3_to_f64(c, lib)
+        r = float(ref[c])
+        assert (math.isnan(got) and math.isnan(r)) or got == r, (c, got, r)
+
+
+def pin_bf16_all_patterns(lib):
+    """Every bf16 bit pattern decodes as torch's bfloat16 decodes it."""
+    allbits = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).to(torch.float64).numpy()
+    for bits in range(0, 65536, 7):
+        got = oracle.bf16_to_f64(bits, lib)
+        r = allbits[bits]
+        assert (math.isnan(got) and math.isnan(r)) or got == r, (bits, got, r)
+
+
+def pin_gather_bruteforce(lib):
+    """Index translation + gather against a plain Python walk, bit-exact.
+
+    Covers masked (-1), negative, >= ctx, page ids past the pool or negative,
+    ragged ctx and duplicates.
+    """
+    for fmt in (W.FMT_FP8, W.FMT_BF16):
+        B = 4
+        ctx = [700, 64, 3, 200]
+        rng = np.random.default_rng(5)
+        idx = np.stack([rng.integers(-3, 720, W.TOPK) for _ in range(B)]).astype(np.int32)
+        idx[2, :5] = [2, 2, 1, 0, 3]
+        w = W.build("g", 902, 0, B, ctx, fmt, "given", topk_idx=idx, max_pages=12)
+        pt = w.page_table.copy()
+        pt[0, 3] = w.pool_pages + 5        # beyond the pool -> masked
+        pt[3, 1] = -2                      # negative page -> masked
+        pool = w.host_pool()
+        # fill the whole pool with non-zero bytes so a wrong row cannot read zeros by luck
+        pool[:] = np.random.default_rng(6).integers(0, 256, pool.size, dtype=np.uint8)
+        slots, rows = oracle.gather(B, W.TOPK, fmt, pool, w.pool_pages, pt, w.topk_idx, w.ctx_len, lib=lib)
+        rb = w.row_bytes
+        for b in range(B):
+            for j in range(W.TOPK):
+                i = int(w.topk_idx[b, j])
+                exp_slot = -1
+                if 0 <= i < ctx[b] and i // 64 < pt.shape[1]:
+                    page = int(pt[b, i // 64])
+                    if 0 <= page < w.pool_pages:
+                        exp_slot = page * 64 + (i - (i // 64) * 64)
+                assert slots[b, j] == exp_slot, (b, j, i, slots[b, j], exp_slot)
+                if exp_slot < 0:
+                    assert not rows[b, j].any()
+                else:
+                    assert np.array_equal(rows[b, j], pool[exp_slot * rb:(exp_slot + 1) * rb])
+
+
+def pin_dense_equals_sdpa(lib):
+    """Selections covering the whole context equal dense attention (torch SDPA, float64)."""
+    for fmt in (W.FMT_FP8, W.FMT_BF16):
+        w = _dense_ws(fmt)
+        pool = w.host_pool()
+        out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+        q = _q64(w)
+        for b in range(w.B):
+            k, v = _torch_rows(fmt, _context_rows(w, pool, b))
+            qb = q[b][None, :, None, :]                       # [1, H, 1, 576]
+            kb = k[None, None].expand(1, W.H, -1, -1)
+            vb = v[None, None].expand(1, W.H, -1, -1)
+            ref = torch.nn.functional.scaled_dot_product_attention(qb, kb, vb, scale=float(w.scale))
+            ref = ref[0, :, 0, :].numpy()
+            ref_lse = torch.logsumexp(float(w.scale) * (q[b] @ k.T), dim=1).numpy()
+            assert np.abs(out[b] - ref).max() <= TOL * max(1.0, np.abs(ref).max()), (fmt, b)
+            assert np.abs(lse[b] - ref_lse).max() <= TOL * 10, (fmt, b)
+
+
+def pin_single_token(lib):
+    """One valid token: out = V_t exactly, lse = scaled score of that token."""
+    for fmt in (W.FMT_FP8, W.FMT_BF16):
+        idx = np.full((2, W.TOPK), -1, np.int32)
+        idx[0, 77] = 1000
+        idx[1, 3] = 5
+        w = W.build("one", 903, fmt, 2, [4096, 6], fmt, "given", topk_idx=idx)
+        pool = w.host_pool()
+        out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+        q = _q64(w).numpy()
+        for b in range(2):
+            k, v = _torch_rows(fmt, _valid_rows(w, pool, b))
+            assert np.array_equal(out[b], np.broadcast_to(v.numpy()[0], (W.H, 512))), (fmt, b)
+            s = float(w.scale) * np.dot(q[b], k.numpy()[0])
+            assert np.abs(lse[b] - s).max() <= 1e-12 * max(1, np.abs(s).max()), (fmt, b)
+
+
+def pin_q_zero(lib):
+    """q = 0: every score is 0, so out = mean of the valid V rows and lse = ln(n_valid)."""
+    for fmt in (W.FMT_FP8, W.FMT_BF16):
+        w = W.build("q0", 904, fmt, 3, [4096, 100, 600], fmt, "uniform", q_zero=True)
+        pool = w.host_pool()
+        out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+        for b in range(3):
+            _, v = _torch_rows(fmt, _valid_rows(w, pool, b))
+            n = v.shape[0]
+            assert np.allclose(out[b], np.broadcast_to(v.numpy().mean(axis=0), (W.H, 512)), rtol=0, atol=1e-13)
+            assert np.allclose(lse[b], math.log(n), rtol=0, atol=1e-13), (b, n)
+
+
+def pin_two_tokens(lib):
+    """Two tokens: weights are the logistic function of the score difference."""
+    idx = np.full((1, W.TOPK), -1, np.int32)
+    idx[0, 10], idx[0, 400] = 7, 130
+    w = W.build("two", 905, W.FMT_FP8, 1, [200], W.FMT_FP8, "given", topk_idx=idx)
+    pool = w.host_pool()
+    out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+    k, v = _torch_rows(W.FMT_FP8, _valid_rows(w, pool, 0))
+    q = _q64(w).numpy()[0]
+    s = float(w.scale) * (q @ k.numpy().T)                   # [H, 2]
+    a = 1.0 / (1.0 + np.exp(s[:, 1] - s[:, 0]))
+    ref = a[:, None] * v.numpy()[0][None] + (1 - a)[:, None] * v.numpy()[1][None]
+    assert np.abs(out[0] - ref).max() <= 1e-12
+    ref_lse = np.maximum(s[:, 0], s[:, 1]) + np.log1p(np.exp(-np.abs(s[:, 0] - s[:, 1])))
+    assert np.abs(lse[0] - ref_lse).max() <= 1e-12
+
+
+def pin_permutation_and_mask_invariance(lib):
+    """Permuting the top-k list (with its -1s) or adding masked slots changes nothing."""
+    w = W.build("perm", 906, 0, 3, [5000, 700, 300], W.FMT_FP8, "uniform")
+    pool = w.host_pool()
+    out0, lse0 = oracle.decode_workload(w, lib=lib, pool=pool)
+    rng = np.random.default_rng(3)
+    idx = w.topk_idx.copy()
+    for b in range(w.B):
+        idx[b] = idx[b][rng.permutation(W.TOPK)]
+    out1, lse1 = oracle.decode(w.q, w.kv_format, pool, w.pool_pages, w.page_table, idx, w.ctx_len, w.scale, lib=lib)
+    assert np.abs(out1 - out0).max() <= 1e-12 and np.abs(lse1 - lse0).max() <= 1e-12
+    # masking slots (with -1, with a value >= ctx, with another negative value)
+    # equals selecting only the remaining tokens, packed in another order
+    keep = w.topk_idx.copy()
+    keep[:, 400:] = -1
+    keep[0, 390:400] = w.ctx_len[0] + 3
+    keep[1, 380:390] = -77
+    outm, lsem = oracle.decode(w.q, w.kv_format, pool, w.pool_pages, w.page_table, keep, w.ctx_len, w.scale, lib=lib)
+    sel = np.full_like(keep, -1)
+    for b in range(w.B):
+        kept = [int(i) for i in keep[b] if 0 <= i < w.ctx_len[b]]
+        sel[b, :len(kept)] = kept
+        sel[b] = sel[b][rng.permutation(W.TOPK)]
+    outs, lses = oracle.decode(w.q, w.kv_format, pool, w.pool_pages, w.page_table, sel, w.ctx_len, w.scale, lib=lib)
+    assert np.abs(outm - outs).max() <= 1e-12 and np.abs(lsem - lses).max() <= 1e-12
+    assert np.abs(outm - out0).max() > 1e-6          # masking really removed tokens
+
+
+def pin_page_relabel(lib):
+    """Relabelling physical pages (pool permuted to match) changes nothing."""
+    w = W.build("relabel", 907, 0, 2, [3000, 4096], W.FMT_FP8, "uniform")
+    pool = w.host_pool()
+    out0, lse0 = oracle.decode_workload(w, lib=lib, pool=pool)
+    P = w.pool_pages
+    perm = np.random.default_rng(9).permutation(P)       # old page p -> new page perm[p]
+    page_bytes = W.PAGE * w.row_bytes
+    pool2 = np.zeros_like(pool)
+    pool2.reshape(P, page_bytes)[perm] = pool.reshape(P, page_bytes)
+    pt2 = perm[w.page_table].astype(np.int32)
+    out1, lse1 = oracle.decode(w.q, w.kv_format, pool2, P, pt2, w.topk_idx, w.ctx_len, w.scale, lib=lib)
+    assert np.array_equal(out1, out0) and np.array_equal(lse1, lse0)
+
+
+def pin_scale_doubling(lib):
+    """With q's latent half zero, doubling every block scale doubles out and keeps lse;
+    with q's rope half zero, scaling one block's scale scales that block of V only."""
+    w = W.build("dbl", 908, 0, 2, [2048, 900], W.FMT_FP8, "uniform")
+    q = w.q.copy()
+    q[:, :, :512] = 0
+    pool = w.host_pool()
+    out0, lse0 = oracle.decode(q, w.kv_format, pool, w.pool_pages, w.page_table, w.topk_idx, w.ctx_len, w.scale, lib=lib)
+    pool2 = pool.copy()
+    rows = pool2.reshape(-1, w.row_bytes)
+    sc = rows[w.row_slots, 512:528].copy().view("<f4") * np.float32(2)
+    rows[w.row_slots, 512:528] = sc.view(np.uint8)
+    out1, lse1 = oracle.decode(q, w.kv_format, pool2, w.pool_pages, w.page_table, w.topk_idx, w.ctx_len, w.scale, lib=lib)
+    assert np.array_equal(out1, 2 * out0)
+    assert np.abs(lse1 - lse0).max() <= 1e-13
+    # only block 2's scale changes; rope-only scores stay, V block 2 scales by 4
+    pool3 = pool.copy()
+    rows3 = pool3.reshape(-1, w.row_bytes)
+    s3 = rows3[w.row_slots, 512:528].copy().view("<f4").reshape(-1, 4)
+    s3[:, 2] *= np.float32(4)
+    rows3[w.row_slots, 512:528] = s3.reshape(-1).view(np.uint8).reshape(-1, 16)
+    out3, lse3 = oracle.decode(q, w.kv_format, pool3, w.pool_pages, w.page_table, w.topk_idx, w.ctx_len, w.scale, lib=lib)
+    assert np.array_equal(out3[:, :, 256:384], 4 * out0[:, :, 256:384])
+    assert np.array_equal(out3[:, :, :256], out0[:, :, :256]) and np.array_equal(out3[:, :, 384:], out0[:, :, 384:])
+    assert np.abs(lse3 - lse0).max() <= 1e-13
+
+
+def pin_split_merge(lib):
+    """Any partition of the selection, merged with the LSE rule, equals the whole (fp64)."""
+    w = W.build("split", 909, 0, 2, [9000, 800], W.FMT_FP8, "uniform")
+    pool = w.host_pool()
+    out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+    rng = np.random.default_rng(4)
+    for nsplit in (2, 3, 7):
+        part = rng.integers(0, nsplit, W.TOPK)
+        outs, lses = [], []
+        for s in range(nsplit):
+            idx = np.where(part[None] == s, w.topk_idx, -1).astype(np.int32)
+            o, l = oracle.decode(w.q, w.kv_format, pool, w.pool_pages, w.page_table, idx, w.ctx_len, w.scale, lib=lib)
+            outs.append(o)
+            lses.append(l)
+        L = np.stack(lses)                                   # [S, B, H]
+        M = L.max(axis=0)
+        wgt = np.exp(L - M[None])
+        merged = (wgt[..., None] * np.stack(outs)).sum(axis=0) / wgt.sum(axis=0)[..., None]
+        assert np.abs(merged - out).max() <= 1e-12
+        assert np.abs(M + np.log(wgt.sum(axis=0)) - lse).max() <= 1e-12
+
+
+def pin_empty_selection(lib):
+    """No valid slot: out = 0 and lse = -inf (never NaN)."""
+    idx = np.full((2, W.TOPK), -1, np.int32)
+    idx[1, :3] = [900, 901, 5000]        # all >= ctx
+    w = W.build("empty", 910, 0, 2, [600, 800], W.FMT_FP8, "given", topk_idx=idx)
+    out, lse = oracle.decode_workload(w, lib=lib)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def pin_bruteforce_tiny(lib):
+    """B=2, ctx=64 (one page), against a pure-Python restatement with math.exp."""
+    for fmt in (W.FMT_FP8, W.FMT_BF16):
+        w = W.build("tiny", 911, fmt, 2, [64, 40], fmt, "uniform")
+        pool = w.host_pool()
+        out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+        q = _q64(w).numpy()
+        for b in range(2):
+            k, v = _torch_rows(fmt, _valid_rows(w, pool, b))
+            k, v = k.numpy().tolist(), v.numpy().tolist()
+            for h in (0, 17, 63):
+                sc = [float(w.scale) * sum(q[b, h, d] * kt[d] for d in range(576)) for kt in k]
+                m = max(sc)
+                ex = [math.exp(x - m) for x in sc]
+                L = sum(ex)
+                ref = [sum(ex[t] * v[t][d] for t in range(len(v))) / L for d in range(512)]
+                assert max(abs(a - r) for a, r in zip(out[b, h], ref)) <= 1e-12, (fmt, b, h)
+                assert abs(lse[b, h] - (m + math.log(L))) <= 1e-12
+
+
+def pin_head_and_request_order(lib):
+    """Each (request, head) uses its own q row: swapping two requests' inputs swaps outputs."""
+    w = W.build("order", 912, 0, 3, [3000, 3000, 3000], W.FMT_FP8, "uniform")
+    pool = w.host_pool()
+    out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+    perm = [2, 0, 1]
+    hperm = np.random.default_rng(2).permutation(W.H)
+    q2 = w.q[perm][:, hperm]
+    out2, lse2 = oracle.decode(q2, w.kv_format, pool, w.pool_pages, w.page_table[perm], w.topk_idx[perm],
+                               w.ctx_len[perm], w.scale, lib=lib)
+    assert np.array_equal(out2, out[perm][:, hperm]) and np.array_equal(lse2, lse[perm][:, hperm])
+
+
+ALL_PINS = [
+    pin_e4m3_all_codes, pin_bf16_all_patterns, pin_gather_bruteforce, pin_dense_equals_sdpa,
+    pin_single_token, pin_q_zero, pin_two_tokens, pin_permutation_and_mask_invariance,
+    pin_page_relabel, pin_scale_doubling, pin_split_merge, pin_empty_selection,
+    pin_bruteforce_tiny, pin_head_and_request_order,
+]
