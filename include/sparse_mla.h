@@ -1,0 +1,186 @@
+/*
+ * sparse_mla.h -- C ABI of libsparse_mla.so: sparse-MLA decode attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (DeepSeek-V4-Flash decode attention as the pages describe it):
+ * each request has 64 query heads; an indexer has selected up to 512 token
+ * positions ("index_topk = 512") of a paged latent KV cache; every head
+ * attends over those selected rows only ("Inside the Decode Performance
+ * Investigation ...", section "The Setup"; "The 64-Block Barrier ...",
+ * section "The Smoking Gun": gather, matrix-vector multiply, accumulation over
+ * the 512 top-k tokens).  The work is split across the top-k dimension and the
+ * partial results are merged with an online-softmax (log-sum-exp) combine
+ * ("The 64-Block Barrier", section "The Split-K Prescription"; "The Commit That
+ * Rewrote the Bottleneck", section "The Levers").
+ *
+ * Definition computed (per request b, head h), with x_t the dequantised
+ * 576-dim cache row of selected token t (512 latent + 64 rope) and v_t its
+ * 512 latent dims:
+ *     s_t = scale * <q[b,h,:], x_t>
+ *     out[b,h,:] = sum_t exp(s_t - m) v_t / sum_t exp(s_t - m),   m = max_t s_t
+ *     lse[b,h]   = ln sum_t exp(s_t)           (natural log of scaled scores)
+ *     no selected token: out = 0, lse = -inf.
+ *
+ * Memory conventions (all pointers are caller-owned):
+ *   - Device pointers are marked [device]; they must be valid on the current
+ *     HIP device.  Host pointers are marked [host].
+ *   - All arrays are dense, row-major, without padding.
+ *   - Nothing is allocated per call.  Calls are asynchronous and ordered on
+ *     `stream` (a hipStream_t; NULL = the default stream); on success the host
+ *     does not wait for the GPU.  Inputs are only read.
+ *   - Errors are detected before any launch and leave every output untouched.
+ *     No C++ exception crosses this interface.
+ *   - The library keeps no per-call state; concurrent calls on different
+ *     streams are safe when their output and workspace buffers are disjoint.
+ */
+#ifndef SPARSE_MLA_H
+#define SPARSE_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed problem constants (the pages: 64 query heads, index_topk = 512). */
+#define SMLA_NUM_HEADS 64
+#define SMLA_D_QK 576       /* 512 latent + 64 rope                        */
+#define SMLA_D_V 512        /* values are the latent dims                  */
+#define SMLA_TOPK 512
+#define SMLA_PAGE_SIZE 64   /* tokens per cache page                       */
+
+/* Cache row formats.  The pool is a flat array of rows; physical page p
+ * holds rows p*64 .. p*64+63 (slot = page*64 + row). */
+typedef enum {
+    SMLA_KV_BF16 = 0,          /* 576 bf16: latent d0..d511, rope r0..r63 (1152 B)          */
+    SMLA_KV_FP8_E4M3_B128 = 1  /* 512 OCP e4m3fn codes | 4 fp32 scales (scale j covers
+                                  dims 128j..128j+127, little-endian) | 64 bf16 rope (656 B) */
+} smla_kv_format;
+
+/* Return codes. */
+#define SMLA_OK 0
+#define SMLA_ERR_INVALID_ARG (-1)       /* null pointer, negative size, bad enum           */
+#define SMLA_ERR_UNSUPPORTED_SHAPE (-2) /* heads != 64, d != 576/512, topk != 512, page != 64 */
+#define SMLA_ERR_WORKSPACE (-3)         /* workspace NULL or smaller than smla_plan_for says */
+#define SMLA_ERR_PLAN (-4)              /* an override plan outside the supported values    */
+#define SMLA_ERR_HIP (-5)               /* a HIP runtime call failed                        */
+
+typedef struct {
+    int32_t batch;             /* B >= 0 requests                                   */
+    int32_t num_heads;         /* must be 64                                        */
+    int32_t d_qk;              /* must be 576                                       */
+    int32_t d_v;               /* must be 512                                       */
+    int32_t topk;              /* must be 512                                       */
+    int32_t page_size;         /* must be 64                                        */
+    int32_t max_pages_per_req; /* >= 1: row stride of page_table                    */
+    int32_t kv_format;         /* smla_kv_format                                    */
+    int64_t pool_pages;        /* >= 1: pages in kv_pool                            */
+} smla_shape;
+
+/* Launch plan.  Zero fields mean "choose automatically". */
+typedef struct {
+    int32_t nsplit;       /* top-k splits per request (1..16); 1 = no combine kernel      */
+    int32_t tile_tokens;  /* tokens per pipeline tile (only 32 is supported)              */
+    int32_t heads_per_wg; /* query heads per workgroup (only 64 is supported)             */
+    int32_t wg_per_cu;    /* resident workgroups per compute unit assumed by the selector */
+} smla_plan;
+
+/*
+ * smla_plan_for -- choose the launch plan for `shape` on the current device and
+ * report the workspace the decode call needs.
+ *   shape            [host] problem description (validated as in sparse_mla_decode)
+ *   override_or_null [host] non-zero fields force those plan values (tests, sweeps)
+ *   out              [host] receives the complete plan
+ *   workspace_bytes  [host] receives the bytes sparse_mla_decode needs (0 if nsplit = 1)
+ * The plan depends only on the shape and the device, never on tensor contents,
+ * so a call sequence can be captured into a HIP graph.
+ * The split count follows the pages' lever of choosing NSPLIT so the grid fills
+ * whole dispatch rounds ("Inside the Decode Performance Investigation",
+ * section "Task 1"; "The Commit That Rewrote the Bottleneck", section "The
+ * Levers"), with this device's compute-unit count.
+ */
+int smla_plan_for(const smla_shape* shape, const smla_plan* override_or_null, smla_plan* out,
+                  size_t* workspace_bytes);
+
+/*
+ * smla_plan_for_cus -- smla_plan_for for a device with `num_cus` compute units,
+ * without touching the GPU (host-only; used by tests and planning tools).
+ */
+int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null, int num_cus,
+                      smla_plan* out, size_t* workspace_bytes);
+
+/*
+ * sparse_mla_decode -- the attention defined at the top of this header.
+ *   q          [device] bf16 [B, 64, 576]
+ *   kv_pool    [device] u8   [pool_pages * 64 * row_bytes]  (row format = shape->kv_format)
+ *   page_table [device] i32  [B, max_pages_per_req]: logical page -> physical page
+ *   topk_idx   [device] i32  [B, 512]: logical token positions.  A slot is masked
+ *                              (contributes nothing) when its index is outside
+ *                              [0, ctx_len[b]), when index/64 >= max_pages_per_req, or
+ *                              when its page id is outside [0, pool_pages).  Duplicate
+ *                              indices count once per slot.
+ *   ctx_len    [device] i32  [B]
+ *   scale      softmax scale applied to <q, x> (e.g. 1/sqrt(576))
+ *   out        [device] bf16 [B, 64, 512]  (round-to-nearest-even from fp32)
+ *   lse        [device] fp32 [B, 64]
+ *   shape      [host]   problem description
+ *   plan_or_null [host] NULL = automatic plan; else as for smla_plan_for's override
+ *   workspace  [device] scratch of at least the size smla_plan_for reports
+ *                        (may be NULL when that size is 0); contents are clobbered
+ *   stream     hipStream_t (NULL = default stream)
+ * Returns SMLA_OK or a negative SMLA_ERR_* code.
+ */
+int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_table,
+                      const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
+                      float* lse, const smla_shape* shape, const smla_plan* plan_or_null,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * smla_decode_split / smla_decode_combine -- the two stages of
+ * sparse_mla_decode as separate calls (a split kernel per (request, top-k
+ * split), then the log-sum-exp combine kernel), for callers that schedule or
+ * time the stages themselves ("Inside the Decode Performance Investigation",
+ * sections "Task 1" and "Task 2": one split and one combine kernel per layer).
+ *   smla_decode_split takes exactly the arguments of sparse_mla_decode.  With
+ *   nsplit = 1 it writes out/lse itself; otherwise it fills the workspace with
+ *   per-split partials (fp32 [B, nsplit, 64, 512] normalised outputs, then fp32
+ *   [B, nsplit, 64] lse at the next 256-byte boundary) and leaves out/lse alone.
+ *   smla_decode_combine merges those partials into out/lse; the same shape and
+ *   plan must be passed, and it does nothing when the plan has nsplit = 1.
+ * Both return as sparse_mla_decode does.
+ */
+int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_table,
+                      const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
+                      float* lse, const smla_shape* shape, const smla_plan* plan_or_null,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, const void* workspace,
+                        size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * smla_gather_rows -- test hook: the index translation and row gather stage of
+ * the decode, on its own ("Inside the Decode Performance Investigation",
+ * section "Task 1": scattered FP8 page gathers).
+ *   kv_pool, page_table, topk_idx, ctx_len, shape: as for sparse_mla_decode
+ *   rows  [device] u8  [B, 512, row_bytes]: the selected rows' bytes, zeros when masked
+ *   slots [device] i64 [B, 512]: physical slot (page*64 + row), -1 when masked
+ * Uses the same device functions as the decode kernel.  Returns as above.
+ */
+int smla_gather_rows(const void* kv_pool, const int32_t* page_table, const int32_t* topk_idx,
+                     const int32_t* ctx_len, const smla_shape* shape, void* rows, int64_t* slots,
+                     void* stream);
+
+/* Bytes per cache row for a format (1152, 656), or -1. */
+int smla_row_bytes(int kv_format);
+
+/* Static description of an error code (never NULL). */
+const char* smla_strerror(int code);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int smla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_MLA_H */

@@ -1,0 +1,198 @@
+"""sparse_mla_top_amd -- sparse-MLA decode attention on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of `libsparse_mla.so` (declared in
+include/sparse_mla.h).  Every step of the decode runs in the library's HIP
+kernels; this module only marshals torch device tensors into pointers and the
+current HIP stream.  There is no CPU fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first; the library then binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_mla.so")
+
+NUM_HEADS = 64
+D_QK = 576
+D_V = 512
+TOPK = 512
+PAGE_SIZE = 64
+KV_BF16 = 0
+KV_FP8 = 1
+ROW_BYTES = {KV_BF16: 1152, KV_FP8: 656}
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED_SHAPE = -2
+ERR_WORKSPACE = -3
+ERR_PLAN = -4
+ERR_HIP = -5
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("topk", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_req", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+                ("pool_pages", ctypes.c_int64)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("nsplit", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
+                ("heads_per_wg", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32p, i64p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        L.smla_plan_for.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Plan), ctypes.POINTER(Plan),
+                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.smla_plan_for.restype = ctypes.c_int
+        L.smla_plan_for_cus.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Plan), ctypes.c_int,
+                                        ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_size_t)]
+        L.smla_plan_for_cus.restype = ctypes.c_int
+        L.sparse_mla_decode.argtypes = [vp, vp, i32p, i32p, i32p, ctypes.c_float, vp, vp,
+                                        ctypes.POINTER(Shape), ctypes.POINTER(Plan), vp, ctypes.c_size_t, vp]
+        L.sparse_mla_decode.restype = ctypes.c_int
+        L.smla_decode_split.argtypes = L.sparse_mla_decode.argtypes
+        L.smla_decode_split.restype = ctypes.c_int
+        L.smla_decode_combine.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Plan), vp, ctypes.c_size_t, vp, vp, vp]
+        L.smla_decode_combine.restype = ctypes.c_int
+        L.smla_gather_rows.argtypes = [vp, i32p, i32p, i32p, ctypes.POINTER(Shape), vp, i64p, vp]
+        L.smla_gather_rows.restype = ctypes.c_int
+        L.smla_row_bytes.argtypes = [ctypes.c_int]
+        L.smla_row_bytes.restype = ctypes.c_int
+        L.smla_strerror.argtypes = [ctypes.c_int]
+        L.smla_strerror.restype = ctypes.c_char_p
+        L.smla_version.argtypes = []
+        L.smla_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().smla_strerror(int(code)).decode()
+
+
+def make_shape(batch: int, kv_format: int, max_pages_per_req: int, pool_pages: int) -> Shape:
+    return Shape(int(batch), NUM_HEADS, D_QK, D_V, TOPK, PAGE_SIZE, int(max_pages_per_req),
+                 int(kv_format), int(pool_pages))
+
+
+def _plan_arg(plan):
+    if plan is None:
+        return None
+    if isinstance(plan, Plan):
+        return ctypes.byref(plan)
+    if isinstance(plan, dict):
+        return ctypes.byref(Plan(int(plan.get("nsplit", 0)), int(plan.get("tile_tokens", 0)),
+                                 int(plan.get("heads_per_wg", 0)), int(plan.get("wg_per_cu", 0))))
+    return ctypes.byref(Plan(int(plan), 0, 0, 0))     # an int = forced nsplit
+
+
+def plan_for(shape: Shape, plan=None):
+    """(Plan, workspace bytes) on the current device."""
+    out, ws = Plan(), ctypes.c_size_t(0)
+    rc = lib().smla_plan_for(ctypes.byref(shape), _plan_arg(plan), ctypes.byref(out), ctypes.byref(ws))
+    if rc != OK:
+        raise SmlaError(rc, "smla_plan_for")
+    return out, int(ws.value)
+
+
+def plan_for_cus(shape: Shape, num_cus: int, plan=None):
+    """(Plan, workspace bytes) for a device with `num_cus` compute units (host only)."""
+    out, ws = Plan(), ctypes.c_size_t(0)
+    rc = lib().smla_plan_for_cus(ctypes.byref(shape), _plan_arg(plan), int(num_cus), ctypes.byref(out),
+                                 ctypes.byref(ws))
+    if rc != OK:
+        raise SmlaError(rc, "smla_plan_for_cus")
+    return out, int(ws.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def decode_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape: Shape, plan=None,
+               workspace=None, stream=None) -> int:
+    """sparse_mla_decode on torch tensors; returns the library's status code."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return lib().sparse_mla_decode(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
+                                   float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape), _plan_arg(plan),
+                                   _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream))
+
+
+def split_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape: Shape, plan=None,
+              workspace=None, stream=None) -> int:
+    """smla_decode_split on torch tensors; returns the status code."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return lib().smla_decode_split(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
+                                   float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape), _plan_arg(plan),
+                                   _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream))
+
+
+def combine_raw(shape: Shape, plan, workspace, out, lse, stream=None) -> int:
+    """smla_decode_combine on torch tensors; returns the status code."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return lib().smla_decode_combine(ctypes.byref(shape), _plan_arg(plan), _ptr(workspace),
+                                     ctypes.c_size_t(ws_bytes), _ptr(out), _ptr(lse), _stream(stream))
+
+
+def decode(q, kv_pool, page_table, topk_idx, ctx_len, scale, *, kv_format: int, pool_pages: int,
+           out=None, lse=None, plan=None, workspace=None, stream=None):
+    """Sparse-MLA decode attention.  Returns (out bf16 [B,64,512], lse fp32 [B,64]).
+
+    q bf16 [B,64,576]; kv_pool uint8 [pool bytes]; page_table int32 [B,max_pages];
+    topk_idx int32 [B,512]; ctx_len int32 [B] -- all on the current GPU.
+    """
+    B = q.shape[0]
+    shape = make_shape(B, kv_format, page_table.shape[1], pool_pages)
+    if out is None:
+        out = torch.empty((B, NUM_HEADS, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, NUM_HEADS), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        _, ws = plan_for(shape, plan)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+    rc = decode_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan, workspace, stream)
+    if rc != OK:
+        raise SmlaError(rc, "sparse_mla_decode")
+    return out, lse
+
+
+def gather_rows(kv_pool, page_table, topk_idx, ctx_len, *, kv_format: int, pool_pages: int, stream=None):
+    """Test hook: (rows uint8 [B,512,row_bytes], slots int64 [B,512]) from the gather stage."""
+    B = topk_idx.shape[0]
+    shape = make_shape(B, kv_format, page_table.shape[1], pool_pages)
+    rows = torch.empty((B, TOPK, ROW_BYTES[kv_format]), dtype=torch.uint8, device=topk_idx.device)
+    slots = torch.empty((B, TOPK), dtype=torch.int64, device=topk_idx.device)
+    rc = lib().smla_gather_rows(_ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
+                                ctypes.byref(shape), _ptr(rows), _ptr(slots), _stream(stream))
+    if rc != OK:
+        raise SmlaError(rc, "smla_gather_rows")
+    return rows, slots

@@ -1,0 +1,271 @@
+// smla_host.cpp -- the C ABI of libsparse_mla.so: argument validation, the
+// wave-aware split selector, workspace carving and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/sparse_mla.h"
+#include "smla_internal.h"
+
+using namespace smla;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxBatch = 1 << 20;     // keeps B * 512 and B * nsplit grids far below 2^31
+std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) { *cus = c; return SMLA_OK; }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    return SMLA_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return SMLA_OK;
+}
+
+int check_shape(const smla_shape* s) {
+  if (!s) return SMLA_ERR_INVALID_ARG;
+  if (s->batch < 0 || s->max_pages_per_req < 1 || s->pool_pages < 1) return SMLA_ERR_INVALID_ARG;
+  if (s->kv_format != SMLA_KV_BF16 && s->kv_format != SMLA_KV_FP8_E4M3_B128) return SMLA_ERR_INVALID_ARG;
+  if (s->num_heads != SMLA_NUM_HEADS || s->d_qk != SMLA_D_QK || s->d_v != SMLA_D_V ||
+      s->topk != SMLA_TOPK || s->page_size != SMLA_PAGE_SIZE)
+    return SMLA_ERR_UNSUPPORTED_SHAPE;
+  // slot = page * 64 + row must fit in int64 and the pool in the address space
+  const int64_t rb = s->kv_format == SMLA_KV_BF16 ? kRowBytesBf16 : kRowBytesFp8;
+  if (s->pool_pages > INT64_MAX / (kPage * rb)) return SMLA_ERR_INVALID_ARG;
+  if (s->batch > kMaxBatch) return SMLA_ERR_INVALID_ARG;
+  return SMLA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_for(int B, int nsplit) {
+  if (nsplit <= 1 || B == 0) return 0;
+  const size_t n = (size_t)B * nsplit * kHeads;
+  return align256(n * kDv * sizeof(float)) + align256(n * sizeof(float));
+}
+
+// Estimated time (us) of one call with `nsplit` splits on `cus` compute units.
+// One workgroup is resident per CU (its LDS tiles take most of the 160 KiB),
+// so B * nsplit workgroups run in ceil(B*nsplit / cus) dispatch rounds, each
+// as long as the longest split (chunk tiles of 32 tokens).  Splitting also
+// writes and re-reads a normalised fp32 partial per (request, split, head)
+// and adds the combine launch.  The constants are calibrated on MI355X.
+double est_time_us(int B, int nsplit, int chunk_tiles, int cus) {
+  const double t_fixed = 2.0;     // translation + first-gather latency per workgroup
+  const double t_tile = 0.45;     // one 32-token tile for 64 heads on one CU
+  const double t_comb = 1.5;      // combine launch + latency
+  const double part_bw = 6.0e6;   // bytes per us for partial traffic
+  const int grid = B * nsplit;
+  const int rounds = (grid + cus - 1) / cus;
+  double t = rounds * (t_fixed + chunk_tiles * t_tile);
+  if (nsplit > 1) t += t_comb + 2.0 * grid * (double)kHeads * (kDv + 1) * 4.0 / part_bw;
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+int smla_row_bytes(int kv_format) {
+  if (kv_format == SMLA_KV_BF16) return kRowBytesBf16;
+  if (kv_format == SMLA_KV_FP8_E4M3_B128) return kRowBytesFp8;
+  return -1;
+}
+
+int smla_version(void) { return 100; }
+
+const char* smla_strerror(int code) {
+  switch (code) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_INVALID_ARG: return "invalid argument";
+    case SMLA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (need 64 heads, d_qk 576, d_v 512, topk 512, page 64)";
+    case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SMLA_ERR_PLAN: return "plan override outside the supported values";
+    case SMLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+// Host-only plan selection for a device with `num_cus` compute units.
+int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus, smla_plan* out,
+                      size_t* workspace_bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!out || !workspace_bytes || num_cus < 1) return SMLA_ERR_INVALID_ARG;
+  smla_plan p = {0, kTile, kHeads, 1};
+  if (ov) {
+    if (ov->nsplit < 0 || ov->nsplit > kTiles) return SMLA_ERR_PLAN;
+    if (ov->tile_tokens != 0 && ov->tile_tokens != kTile) return SMLA_ERR_PLAN;
+    if (ov->heads_per_wg != 0 && ov->heads_per_wg != kHeads) return SMLA_ERR_PLAN;
+    if (ov->wg_per_cu < 0 || ov->wg_per_cu > 1) return SMLA_ERR_PLAN;
+    p.nsplit = ov->nsplit;
+  }
+  const int B = shape->batch;
+  const int slots = num_cus * p.wg_per_cu;
+  if (p.nsplit == 0) {
+    double best = INFINITY;
+    int best_ns = 1;
+    for (int ns = 1; ns <= kTiles; ++ns) {
+      const int chunk = (kTiles + ns - 1) / ns;
+      if ((kTiles + chunk - 1) / chunk != ns) continue;   // only split counts with no empty split
+      const double t = est_time_us(B > 0 ? B : 1, ns, chunk, slots);
+      if (t < best - 1e-9) { best = t; best_ns = ns; }
+    }
+    p.nsplit = best_ns;
+  }
+  // normalise: chunk of whole tiles, no empty trailing split
+  const int chunk = (kTiles + p.nsplit - 1) / p.nsplit;
+  p.nsplit = (kTiles + chunk - 1) / chunk;
+  *out = p;
+  *workspace_bytes = workspace_for(B, p.nsplit);
+  return SMLA_OK;
+}
+
+int smla_plan_for(const smla_shape* shape, const smla_plan* ov, smla_plan* out, size_t* workspace_bytes) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc) return rc;
+  return smla_plan_for_cus(shape, ov, cus, out, workspace_bytes);
+}
+
+// Validated launch description shared by the decode entry points.
+struct Prepared {
+  SplitArgs split;
+  CombineArgs combine;
+  int B = 0;
+  int nsplit = 1;
+  int fmt = 0;
+};
+
+static int prepare(const void* q, const void* kv_pool, const int32_t* page_table, const int32_t* topk_idx,
+                   const int32_t* ctx_len, float scale, void* out, float* lse, const smla_shape* shape,
+                   const smla_plan* plan_or_null, void* workspace, size_t workspace_bytes, Prepared* pr) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!q || !kv_pool || !page_table || !topk_idx || !ctx_len || !out || !lse) return SMLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+  const int B = shape->batch;
+  smla_plan plan;
+  size_t need = 0;
+  rc = smla_plan_for(shape, plan_or_null, &plan, &need);
+  if (rc) return rc;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SMLA_ERR_WORKSPACE;
+  if ((need > 0 && ((uintptr_t)workspace & 15)) || ((uintptr_t)q & 15) || ((uintptr_t)kv_pool & 15) ||
+      ((uintptr_t)out & 7))
+    return SMLA_ERR_INVALID_ARG;
+  SplitArgs& a = pr->split;
+  a.q = (const uint16_t*)q;
+  a.pool = (const uint8_t*)kv_pool;
+  a.page_table = page_table;
+  a.topk_idx = topk_idx;
+  a.ctx_len = ctx_len;
+  a.pool_pages = shape->pool_pages;
+  a.max_pages = shape->max_pages_per_req;
+  a.nsplit = plan.nsplit;
+  a.chunk_tiles = (kTiles + plan.nsplit - 1) / plan.nsplit;
+  a.scale_log2 = scale * kLog2e;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  if (plan.nsplit > 1) {
+    const size_t n = (size_t)B * plan.nsplit * kHeads;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((uint8_t*)workspace + align256(n * kDv * sizeof(float)));
+  }
+  CombineArgs& c = pr->combine;
+  c.part_o = a.part_o;
+  c.part_lse = a.part_lse;
+  c.nsplit = plan.nsplit;
+  c.out = (uint16_t*)out;
+  c.lse = lse;
+  pr->B = B;
+  pr->nsplit = plan.nsplit;
+  pr->fmt = shape->kv_format;
+  return SMLA_OK;
+}
+
+int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_table,
+                      const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
+                      float* lse, const smla_shape* shape, const smla_plan* plan_or_null,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Prepared pr;
+  int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
+                   workspace, workspace_bytes, &pr);
+  if (rc || pr.B == 0) return rc;
+  const hipStream_t st = (hipStream_t)stream;
+  if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, st) != hipSuccess) return SMLA_ERR_HIP;
+  if (pr.nsplit > 1 && launch_combine(pr.combine, pr.B, st) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_table,
+                      const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
+                      float* lse, const smla_shape* shape, const smla_plan* plan_or_null,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  Prepared pr;
+  int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
+                   workspace, workspace_bytes, &pr);
+  if (rc || pr.B == 0) return rc;
+  if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, const void* workspace,
+                        size_t workspace_bytes, void* out, float* lse, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!out || !lse) return SMLA_ERR_INVALID_ARG;
+  smla_plan plan;
+  size_t need = 0;
+  rc = smla_plan_for(shape, plan_or_null, &plan, &need);
+  if (rc) return rc;
+  if (shape->batch == 0 || plan.nsplit == 1) return SMLA_OK;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15)) return SMLA_ERR_WORKSPACE;
+  if ((uintptr_t)out & 7) return SMLA_ERR_INVALID_ARG;
+  const size_t n = (size_t)shape->batch * plan.nsplit * kHeads;
+  CombineArgs c;
+  c.part_o = (const float*)workspace;
+  c.part_lse = (const float*)((const uint8_t*)workspace + align256(n * kDv * sizeof(float)));
+  c.nsplit = plan.nsplit;
+  c.out = (uint16_t*)out;
+  c.lse = lse;
+  if (launch_combine(c, shape->batch, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+int smla_gather_rows(const void* kv_pool, const int32_t* page_table, const int32_t* topk_idx,
+                     const int32_t* ctx_len, const smla_shape* shape, void* rows, int64_t* slots,
+                     void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!kv_pool || !page_table || !topk_idx || !ctx_len || !rows || !slots) return SMLA_ERR_INVALID_ARG;
+  if (((uintptr_t)kv_pool & 15) || ((uintptr_t)rows & 15)) return SMLA_ERR_INVALID_ARG;
+  if (shape->batch == 0) return SMLA_OK;
+  GatherArgs g;
+  g.pool = (const uint8_t*)kv_pool;
+  g.page_table = page_table;
+  g.topk_idx = topk_idx;
+  g.ctx_len = ctx_len;
+  g.pool_pages = shape->pool_pages;
+  g.max_pages = shape->max_pages_per_req;
+  g.rows = (uint8_t*)rows;
+  g.slots = slots;
+  if (launch_gather(g, shape->kv_format, shape->batch, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+}  // extern "C"

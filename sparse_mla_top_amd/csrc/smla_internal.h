@@ -1,0 +1,65 @@
+// smla_internal.h -- constants and kernel argument blocks shared by the host
+// launcher code and the kernels of libsparse_mla.so (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kHeads = 64;
+constexpr int kDqk = 576;
+constexpr int kDl = 512;        // latent dims
+constexpr int kDv = 512;
+constexpr int kTopk = 512;
+constexpr int kPage = 64;
+constexpr int kTile = 32;       // tokens per pipeline tile
+constexpr int kTiles = kTopk / kTile;
+constexpr int kThreads = 256;   // 4 waves x 16 heads
+constexpr int kFmtBf16 = 0;
+constexpr int kFmtFp8 = 1;
+constexpr int kRowBytesBf16 = 2 * kDqk;                  // 1152
+constexpr int kRowBytesFp8 = kDl + 16 + 2 * 64;          // 656
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+struct SplitArgs {
+  const uint16_t* q;           // bf16 [B][64][576]
+  const uint8_t* pool;
+  const int32_t* page_table;   // [B][max_pages]
+  const int32_t* topk_idx;     // [B][512]
+  const int32_t* ctx_len;      // [B]
+  int64_t pool_pages;
+  int max_pages;
+  int nsplit;                  // splits per request
+  int chunk_tiles;             // tiles per split (last split may hold fewer)
+  float scale_log2;            // softmax scale * log2(e)
+  float* part_o;               // [B][nsplit][64][512] normalised partial outputs
+  float* part_lse;             // [B][nsplit][64] natural-log lse of each split
+  uint16_t* out;               // bf16 [B][64][512] (written directly when nsplit == 1)
+  float* lse;                  // [B][64]
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  int nsplit;
+  uint16_t* out;
+  float* lse;
+};
+
+struct GatherArgs {
+  const uint8_t* pool;
+  const int32_t* page_table;
+  const int32_t* topk_idx;
+  const int32_t* ctx_len;
+  int64_t pool_pages;
+  int max_pages;
+  uint8_t* rows;
+  int64_t* slots;
+};
+
+hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, int fmt, int B, hipStream_t stream);
+
+}  // namespace smla

@@ -1,0 +1,138 @@
+"""Host-side checks of libsparse_mla.so that need no GPU: exports, validation, selector."""
+from __future__ import annotations
+
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+import sparse_mla_top_amd as smla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_mla.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"sparse_mla_decode", "smla_plan_for", "smla_gather_rows", "smla_strerror"} <= set(names)
+    L = smla.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in sparse_mla.h but not exported"
+
+
+def test_version_and_row_bytes():
+    L = smla.lib()
+    assert L.smla_version() >= 100
+    assert L.smla_row_bytes(smla.KV_BF16) == 1152
+    assert L.smla_row_bytes(smla.KV_FP8) == 656
+    assert L.smla_row_bytes(7) == -1
+    for code in (0, -1, -2, -3, -4, -5, -99):
+        assert smla.strerror(code)
+
+
+def _shape(**kw):
+    s = smla.make_shape(kw.pop("batch", 8), kw.pop("kv_format", smla.KV_FP8), kw.pop("max_pages", 16),
+                        kw.pop("pool_pages", 1024))
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _decode_rc(shape, nonnull=True, scale=1 / 24):
+    # pointers are never dereferenced on these paths: validation fails first
+    p = ctypes.c_void_p(16) if nonnull else None
+    return smla.lib().sparse_mla_decode(p, p, p, p, p, scale, p, p, ctypes.byref(shape), None, None, 0, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_heads", 32, smla.ERR_UNSUPPORTED_SHAPE), ("d_qk", 512, smla.ERR_UNSUPPORTED_SHAPE),
+    ("d_v", 576, smla.ERR_UNSUPPORTED_SHAPE), ("topk", 2048, smla.ERR_UNSUPPORTED_SHAPE),
+    ("page_size", 16, smla.ERR_UNSUPPORTED_SHAPE), ("batch", -1, smla.ERR_INVALID_ARG),
+    ("max_pages_per_req", 0, smla.ERR_INVALID_ARG), ("pool_pages", 0, smla.ERR_INVALID_ARG),
+    ("kv_format", 5, smla.ERR_INVALID_ARG),
+])
+def test_shape_validation(field, value, code):
+    assert _decode_rc(_shape(**{field: value})) == code
+
+
+def test_null_pointers_and_bad_scale():
+    assert _decode_rc(_shape(), nonnull=False) == smla.ERR_INVALID_ARG
+    assert _decode_rc(_shape(), scale=float("nan")) == smla.ERR_INVALID_ARG
+    assert smla.lib().sparse_mla_decode(None, None, None, None, None, 1.0, None, None, None, None, None, 0,
+                                        None) == smla.ERR_INVALID_ARG
+
+
+def test_plan_overrides_validated():
+    s = _shape()
+    for bad in ({"nsplit": 17}, {"nsplit": -1}, {"tile_tokens": 16}, {"heads_per_wg": 32}, {"wg_per_cu": 3}):
+        with pytest.raises(smla.SmlaError) as e:
+            smla.plan_for_cus(s, 256, bad)
+        assert e.value.code == smla.ERR_PLAN
+
+
+@pytest.mark.parametrize("forced,expect", [(1, 1), (2, 2), (3, 3), (5, 4), (6, 6), (7, 6), (9, 8), (16, 16)])
+def test_forced_nsplit_normalised_to_whole_tiles(forced, expect):
+    # splits hold whole 32-token tiles: 16 tiles in chunks of ceil(16/n), no empty split
+    p, ws = smla.plan_for_cus(_shape(batch=8), 256, forced)
+    assert p.nsplit == expect
+    chunk = math.ceil(16 / p.nsplit)
+    assert (p.nsplit - 1) * chunk < 16 <= p.nsplit * chunk
+    assert ws == (0 if expect == 1 else (((8 * expect * 64 * 512 * 4) + 255) // 256 * 256
+                                         + ((8 * expect * 64 * 4) + 255) // 256 * 256))
+
+
+def test_selector_is_shape_only_and_bounded():
+    for B in (1, 8, 16, 32, 48, 64, 80, 88, 96, 300):
+        p, ws = smla.plan_for_cus(_shape(batch=B), 256)
+        assert 1 <= p.nsplit <= 16
+        p2, ws2 = smla.plan_for_cus(_shape(batch=B), 256)
+        assert p.as_dict() == p2.as_dict() and ws == ws2
+    # with many requests the grid already fills the device: no split needed
+    p, _ = smla.plan_for_cus(_shape(batch=2048), 256)
+    assert p.nsplit == 1
+
+
+def test_selector_fills_compute_units_at_small_batch():
+    # at B=1 a single workgroup would idle 255 of 256 CUs
+    p, _ = smla.plan_for_cus(_shape(batch=1), 256)
+    assert p.nsplit >= 8
+
+
+# ---------------------------------------------------------------- pages' grid arithmetic
+GOLDEN = os.path.join(ROOT, "tests", "golden", "pages_grid_arithmetic.json")
+
+
+def pages_nsplit(B: int) -> int:
+    """The NSPLIT rule the pages quote for their sm120 Triton kernel."""
+    return min(16, math.ceil(256 / (B * 2)))
+
+
+def dispatch_rounds(grid: int, slots: int) -> float:
+    return grid / slots
+
+
+def test_pages_worked_grid_numbers():
+    g = json.load(open(GOLDEN))
+    for case in g["nsplit_rule"]:
+        B = case["B"]
+        grid = B * 2 * pages_nsplit(B)
+        assert grid == case["ctas"], case
+        if "rounds" in case:
+            assert round(dispatch_rounds(grid, g["sm_count"]), 2) == case["rounds"], case
+        if "first_round" in case:
+            assert min(grid, g["sm_count"]) == case["first_round"]
+            assert grid - g["sm_count"] == case["second_round"]
+    old = g["unsplit_grid"]
+    assert old["B"] * old["H"] == old["blocks"]
+    assert round(old["blocks"] / old["sms"], 2) == old["occupancy"]
+    sk = g["split_k_target"]
+    assert sk["B"] * sk["H"] * sk["nsplit"] == sk["blocks"]

@@ -1,0 +1,189 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mla_top_amd as smla
+import workloads as W
+from parity import assert_parity, TOL
+from workloads.device import upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _run(d, plan=None):
+    out, lse = smla.decode(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale,
+                           kv_format=d.kv_format, pool_pages=d.pool_pages, plan=plan)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check(w, plan=None, what=None):
+    what = what or f"{w.name} plan={plan}"
+    _say(what)
+    pool = w.host_pool()
+    d = upload(w)
+    out, lse = _run(d, plan)
+    ref_o, ref_l = oracle.decode_workload(w, pool=pool)
+    return assert_parity(out, lse, ref_o, ref_l, what)
+
+
+# --------------------------------------------------------------------------- gather
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_gather_bit_exact(wid):
+    w = W.make(wid)
+    _say(f"gather {w.name}")
+    pool = w.host_pool()
+    d = upload(w)
+    rows, slots = smla.gather_rows(d.pool, d.page_table, d.topk_idx, d.ctx_len, kv_format=d.kv_format,
+                                   pool_pages=d.pool_pages)
+    torch.cuda.synchronize()
+    ref_slots, ref_rows = oracle.gather_workload(w, pool=pool)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert np.array_equal(rows.cpu().numpy(), ref_rows)
+
+
+def test_gather_edge_indices():
+    B = 4
+    rng = np.random.default_rng(8)
+    idx = np.stack([rng.integers(-3, 760, W.TOPK) for _ in range(B)]).astype(np.int32)
+    w = W.build("edge", 920, 0, B, [700, 64, 3, 200], W.FMT_FP8, "given", topk_idx=idx, max_pages=12)
+    w.page_table[0, 3] = w.pool_pages + 5
+    w.page_table[3, 1] = -2
+    _say("gather edge indices")
+    pool = w.host_pool()
+    d = upload(w)
+    rows, slots = smla.gather_rows(d.pool, d.page_table, d.topk_idx, d.ctx_len, kv_format=d.kv_format,
+                                   pool_pages=d.pool_pages)
+    torch.cuda.synchronize()
+    ref_slots, ref_rows = oracle.gather_workload(w, pool=pool)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert np.array_equal(rows.cpu().numpy(), ref_rows)
+
+
+# --------------------------------------------------------------------------- decode
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_decode_workloads(wid):
+    _check(W.make(wid))
+
+
+def test_decode_b1_in_fp8_format():
+    _check(W.make(1, kv_format=W.FMT_FP8))
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
+def test_decode_forced_nsplit(nsplit, fmt):
+    w = W.build("nsplit", 930, fmt, 6, [65536, 4096, 700, 513, 300, 131072], fmt, "uniform")
+    _check(w, plan=nsplit, what=f"forced nsplit={nsplit} fmt={fmt}")
+
+
+def test_nsplit_results_agree():
+    w = W.build("agree", 931, 0, 5, [65536, 4096, 700, 300, 131072], W.FMT_FP8, "uniform")
+    d = upload(w)
+    outs = [(_run(d, ns)) for ns in (1, 2, 4, 8, 16)]
+    o0 = outs[0][0].float()
+    for o, l in outs[1:]:
+        denom = o0.abs().amax(dim=-1).clamp_min(1e-30)
+        assert ((o.float() - o0).abs().amax(dim=-1) / denom).max().item() <= 2 * TOL
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
+def test_sweep_sampled_layers(fmt):
+    """512K-context sweep workload: sampled layers at B = 96 and prefixes."""
+    for layer in (0, 41):
+        w = W.make(5, layer=layer, kv_format=fmt)
+        _check(w, what=f"sweep layer {layer} B=96 fmt={fmt}")
+        for b in (1, 8, 33):
+            _check(w.subset(b), what=f"sweep layer {layer} B={b} fmt={fmt}")
+
+
+def test_masked_and_degenerate_requests():
+    idx = np.full((6, W.TOPK), -1, np.int32)
+    rng = np.random.default_rng(12)
+    idx[1, 100] = 7                                   # single valid token
+    idx[2] = rng.permutation(W.TOPK).astype(np.int32) # dense ctx = 512
+    idx[3, ::2] = rng.choice(5000, 256, replace=False)
+    idx[3, 1::2] = 5000 + rng.integers(0, 100, 256)   # >= ctx -> masked
+    idx[4] = rng.integers(0, 50, W.TOPK)              # duplicates (count per slot)
+    idx[5, 480:] = rng.choice(3000, 32, replace=False)  # only the last tile valid
+    w = W.build("degenerate", 940, 0, 6, [1000, 8, 512, 5000, 50, 3000], W.FMT_FP8, "given", topk_idx=idx)
+    for ns in (1, 4, 16):
+        _check(w, plan=ns, what=f"degenerate nsplit={ns}")
+
+
+def test_q_zero_and_single_token_closed_forms():
+    w = W.build("q0", 941, 0, 3, [4096, 100, 600], W.FMT_FP8, "uniform", q_zero=True)
+    _check(w, plan=4, what="q=0")
+
+
+def test_invalid_page_ids_are_masked():
+    w = W.build("badpages", 942, 0, 3, [3000, 3000, 3000], W.FMT_FP8, "uniform")
+    w.page_table[0, :10] = -5
+    w.page_table[1, 5:20] = w.pool_pages + 100
+    _check(w, plan=2, what="invalid page ids")
+
+
+def test_permutation_invariance_on_gpu():
+    w = W.make(2)
+    d = upload(w)
+    out0, lse0 = _run(d)
+    rng = np.random.default_rng(1)
+    perm = np.stack([rng.permutation(W.TOPK) for _ in range(w.B)])
+    d.topk_idx = torch.from_numpy(np.take_along_axis(w.topk_idx, perm, axis=1)).cuda()
+    out1, lse1 = _run(d)
+    denom = out0.float().abs().amax(dim=-1)
+    assert ((out1.float() - out0.float()).abs().amax(dim=-1) / denom).max().item() <= 2 * TOL
+    assert (lse1 - lse0).abs().max().item() <= 2 * TOL
+
+
+def test_deterministic_rerun():
+    w = W.make(3)
+    d = upload(w)
+    a = _run(d)
+    b = _run(d)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_batch_and_errors():
+    w = W.build("err", 943, 0, 2, [3000, 3000], W.FMT_FP8, "uniform")
+    d = upload(w)
+    shape = smla.make_shape(2, d.kv_format, d.page_table.shape[1], d.pool_pages)
+    out = torch.full((2, 64, 512), 7, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((2, 64), 7, dtype=torch.float32, device="cuda")
+    plan, ws = smla.plan_for(shape, 4)
+    assert ws > 0
+    small = torch.empty(ws - 256, dtype=torch.uint8, device="cuda")
+    rc = smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, out, lse, shape, 4, small)
+    assert rc == smla.ERR_WORKSPACE
+    rc = smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, out, lse, shape, 4, None)
+    assert rc == smla.ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(out == 7) and torch.all(lse == 7)      # outputs untouched on error
+    empty = smla.make_shape(0, d.kv_format, d.page_table.shape[1], d.pool_pages)
+    rc = smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, out, lse, empty)
+    assert rc == smla.OK
+
+
+def test_split_and_combine_stages_equal_decode():
+    w = W.make(2)
+    d = upload(w)
+    shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages)
+    for ns in (1, 4):
+        plan, ws_bytes = smla.plan_for(shape, ns)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        o1 = torch.empty((w.B, 64, 512), dtype=torch.bfloat16, device="cuda")
+        l1 = torch.empty((w.B, 64), dtype=torch.float32, device="cuda")
+        o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+        assert smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o1, l1, shape, ns, ws) == 0
+        assert smla.split_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o2, l2, shape, ns, ws) == 0
+        assert smla.combine_raw(shape, ns, ws, o2, l2) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -251,6 +251,9 @@ def build(name: str, workload_id: int, layer: int, B: int, ctx_len, kv_format: i
     rb = ROW_BYTES[kv_format]
     row_slots = np.concatenate(slots_all) if slots_all else np.zeros(0, np.int64)
     row_data = np.concatenate(data_all) if data_all else np.zeros((0, rb), np.uint8)
+    # a slot selected twice keeps its first row, so every copy of the pool agrees
+    row_slots, first = np.unique(row_slots, return_index=True)
+    row_data = row_data[first]
     return Workload(name=name, kv_format=kv_format, q=q, page_table=pt, topk_idx=idx,
                     ctx_len=ctx.astype(np.int32), pool_pages=pool_pages + page_base,
                     row_slots=row_slots, row_data=row_data)
