@@ -95,7 +95,7 @@ def main() -> int:
     shape = smla.make_shape(B, w0.kv_format, w0.max_pages, pool_pages)
     plan, ws_bytes = smla.plan_for(shape, args.nsplit or None)
     plan_arg = plan
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = smla.new_workspace(ws_bytes, dev)
     out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 64), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()

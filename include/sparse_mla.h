@@ -127,8 +127,16 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *   shape      [host]   problem description
  *   plan_or_null [host] NULL = automatic plan; else as for smla_plan_for's override
  *   workspace  [device] scratch of at least the size smla_plan_for reports
- *                        (may be NULL when that size is 0); contents are clobbered
+ *                        (may be NULL when that size is 0).  It holds the split
+ *                        partials and one arrival counter per request: it must be
+ *                        zero-filled once before its first use (smla_workspace_init),
+ *                        and every successful call leaves the counters at zero again.
+ *                        Calls that share a workspace must not overlap in time.
  *   stream     hipStream_t (NULL = default stream)
+ * The work runs as one kernel launch: each (request, split) workgroup writes
+ * its partial result, and the last split of a request to finish merges them
+ * (the log-sum-exp combine of "The 64-Block Barrier", section "The Split-K
+ * Prescription", fused into the same launch).
  * Returns SMLA_OK or a negative SMLA_ERR_* code.
  */
 int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_table,
@@ -145,7 +153,8 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
  *   smla_decode_split takes exactly the arguments of sparse_mla_decode.  With
  *   nsplit = 1 it writes out/lse itself; otherwise it fills the workspace with
  *   per-split partials (fp32 [B, nsplit, 64, 512] normalised outputs, then fp32
- *   [B, nsplit, 64] lse at the next 256-byte boundary) and leaves out/lse alone.
+ *   [B, nsplit, 64] lse at the next 256-byte boundary) and leaves out/lse and
+ *   the arrival counters alone.
  *   smla_decode_combine merges those partials into out/lse; the same shape and
  *   plan must be passed, and it does nothing when the plan has nsplit = 1.
  * Both return as sparse_mla_decode does.
@@ -169,6 +178,13 @@ int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, 
 int smla_gather_rows(const void* kv_pool, const int32_t* page_table, const int32_t* topk_idx,
                      const int32_t* ctx_len, const smla_shape* shape, void* rows, int64_t* slots,
                      void* stream);
+
+/*
+ * smla_workspace_init -- zero a workspace (its arrival counters) on `stream`
+ * with a fill kernel, before its first use by sparse_mla_decode, or after a
+ * call that did not complete.  workspace [device], 4-byte aligned.
+ */
+int smla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes per cache row for a format (1152, 656), or -1. */
 int smla_row_bytes(int kv_format);

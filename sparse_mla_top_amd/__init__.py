@@ -77,6 +77,8 @@ def lib():
         L.smla_decode_split.restype = ctypes.c_int
         L.smla_decode_combine.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Plan), vp, ctypes.c_size_t, vp, vp, vp]
         L.smla_decode_combine.restype = ctypes.c_int
+        L.smla_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
+        L.smla_workspace_init.restype = ctypes.c_int
         L.smla_gather_rows.argtypes = [vp, i32p, i32p, i32p, ctypes.POINTER(Shape), vp, i64p, vp]
         L.smla_gather_rows.restype = ctypes.c_int
         L.smla_row_bytes.argtypes = [ctypes.c_int]
@@ -138,9 +140,29 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _check_tensors(shape: Shape, q, kv_pool, page_table, topk_idx, ctx_len, out, lse):
+    """Raise if a tensor is smaller than `shape` says (the kernels trust the shape)."""
+    B = int(shape.batch)
+    if B <= 0:
+        return
+    rb = ROW_BYTES.get(int(shape.kv_format))
+    need = [(q, B * NUM_HEADS * D_QK * 2, "q"), (page_table, B * int(shape.max_pages_per_req) * 4, "page_table"),
+            (topk_idx, B * TOPK * 4, "topk_idx"), (ctx_len, B * 4, "ctx_len"),
+            (out, B * NUM_HEADS * D_V * 2, "out"), (lse, B * NUM_HEADS * 4, "lse")]
+    if rb is not None:
+        need.append((kv_pool, int(shape.pool_pages) * PAGE_SIZE * rb, "kv_pool"))
+    for t, nbytes, name in need:
+        if t is None:
+            continue
+        have = t.numel() * t.element_size()
+        if have < nbytes or not t.is_contiguous():
+            raise ValueError(f"{name}: {have} bytes (contiguous={t.is_contiguous()}) but the shape needs {nbytes}")
+
+
 def decode_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape: Shape, plan=None,
                workspace=None, stream=None) -> int:
     """sparse_mla_decode on torch tensors; returns the library's status code."""
+    _check_tensors(shape, q, kv_pool, page_table, topk_idx, ctx_len, out, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return lib().sparse_mla_decode(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
                                    float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape), _plan_arg(plan),
@@ -150,6 +172,7 @@ def decode_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape
 def split_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape: Shape, plan=None,
               workspace=None, stream=None) -> int:
     """smla_decode_split on torch tensors; returns the status code."""
+    _check_tensors(shape, q, kv_pool, page_table, topk_idx, ctx_len, out, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return lib().smla_decode_split(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
                                    float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape), _plan_arg(plan),
@@ -161,6 +184,20 @@ def combine_raw(shape: Shape, plan, workspace, out, lse, stream=None) -> int:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return lib().smla_decode_combine(ctypes.byref(shape), _plan_arg(plan), _ptr(workspace),
                                      ctypes.c_size_t(ws_bytes), _ptr(out), _ptr(lse), _stream(stream))
+
+
+def new_workspace(nbytes: int, device=None, stream=None):
+    """A zero-initialised workspace of `nbytes` (at least 256) for sparse_mla_decode."""
+    ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+    return ws
+
+
+def workspace_init(workspace, stream=None) -> None:
+    """Zero a workspace's arrival counters on the stream (fill kernel)."""
+    rc = lib().smla_workspace_init(_ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                   _stream(stream))
+    if rc != OK:
+        raise SmlaError(rc, "smla_workspace_init")
 
 
 def decode(q, kv_pool, page_table, topk_idx, ctx_len, scale, *, kv_format: int, pool_pages: int,
@@ -178,7 +215,7 @@ def decode(q, kv_pool, page_table, topk_idx, ctx_len, scale, *, kv_format: int, 
         lse = torch.empty((B, NUM_HEADS), dtype=torch.float32, device=q.device)
     if workspace is None:
         _, ws = plan_for(shape, plan)
-        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(ws, q.device)
     rc = decode_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan, workspace, stream)
     if rc != OK:
         raise SmlaError(rc, "sparse_mla_decode")
@@ -189,6 +226,7 @@ def gather_rows(kv_pool, page_table, topk_idx, ctx_len, *, kv_format: int, pool_
     """Test hook: (rows uint8 [B,512,row_bytes], slots int64 [B,512]) from the gather stage."""
     B = topk_idx.shape[0]
     shape = make_shape(B, kv_format, page_table.shape[1], pool_pages)
+    _check_tensors(shape, None, kv_pool, page_table, topk_idx, ctx_len, None, None)
     rows = torch.empty((B, TOPK, ROW_BYTES[kv_format]), dtype=torch.uint8, device=topk_idx.device)
     slots = torch.empty((B, TOPK), dtype=torch.int64, device=topk_idx.device)
     rc = lib().smla_gather_rows(_ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),

@@ -49,10 +49,14 @@ int check_shape(const smla_shape* s) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace layout (nsplit > 1): fp32 partial outputs [B, nsplit, 64, 512],
+// fp32 partial lse [B, nsplit, 64], uint32 arrival counters [B]; each region
+// starts at a 256-byte boundary.
+size_t ws_part_o_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * kDv * sizeof(float)); }
+size_t ws_part_lse_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * sizeof(float)); }
 size_t workspace_for(int B, int nsplit) {
   if (nsplit <= 1 || B == 0) return 0;
-  const size_t n = (size_t)B * nsplit * kHeads;
-  return align256(n * kDv * sizeof(float)) + align256(n * sizeof(float));
+  return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * sizeof(uint32_t));
 }
 
 // Estimated time (us) of one call with `nsplit` splits on `cus` compute units.
@@ -181,10 +185,11 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   a.lse = lse;
   a.part_o = nullptr;
   a.part_lse = nullptr;
+  a.counters = nullptr;
   if (plan.nsplit > 1) {
-    const size_t n = (size_t)B * plan.nsplit * kHeads;
     a.part_o = (float*)workspace;
-    a.part_lse = (float*)((uint8_t*)workspace + align256(n * kDv * sizeof(float)));
+    a.part_lse = (float*)((uint8_t*)workspace + ws_part_o_bytes(B, plan.nsplit));
+    a.counters = (uint32_t*)((uint8_t*)workspace + ws_part_o_bytes(B, plan.nsplit) + ws_part_lse_bytes(B, plan.nsplit));
   }
   CombineArgs& c = pr->combine;
   c.part_o = a.part_o;
@@ -206,9 +211,8 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
   int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
-  const hipStream_t st = (hipStream_t)stream;
-  if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, st) != hipSuccess) return SMLA_ERR_HIP;
-  if (pr.nsplit > 1 && launch_combine(pr.combine, pr.B, st) != hipSuccess) return SMLA_ERR_HIP;
+  // one launch: the last split of each request merges the partials
+  if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 
@@ -220,6 +224,7 @@ int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_ta
   int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
+  pr.split.counters = nullptr;          // partials only; smla_decode_combine merges them
   if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
@@ -236,14 +241,19 @@ int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, 
   if (shape->batch == 0 || plan.nsplit == 1) return SMLA_OK;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15)) return SMLA_ERR_WORKSPACE;
   if ((uintptr_t)out & 7) return SMLA_ERR_INVALID_ARG;
-  const size_t n = (size_t)shape->batch * plan.nsplit * kHeads;
   CombineArgs c;
   c.part_o = (const float*)workspace;
-  c.part_lse = (const float*)((const uint8_t*)workspace + align256(n * kDv * sizeof(float)));
+  c.part_lse = (const float*)((const uint8_t*)workspace + ws_part_o_bytes(shape->batch, plan.nsplit));
   c.nsplit = plan.nsplit;
   c.out = (uint16_t*)out;
   c.lse = lse;
   if (launch_combine(c, shape->batch, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+int smla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || ((uintptr_t)workspace & 3)) return workspace_bytes == 0 ? SMLA_OK : SMLA_ERR_INVALID_ARG;
+  if (launch_zero((uint32_t*)workspace, workspace_bytes / 4, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 

@@ -14,7 +14,8 @@ constexpr int kTopk = 512;
 constexpr int kPage = 64;
 constexpr int kTile = 32;       // tokens per pipeline tile
 constexpr int kTiles = kTopk / kTile;
-constexpr int kThreads = 256;   // 4 waves x 16 heads
+constexpr int kWaves = 8;       // split kernel: 4 QK waves + 4 PV waves
+constexpr int kThreads = 64 * kWaves;
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;
 constexpr int kRowBytesBf16 = 2 * kDqk;                  // 1152
@@ -37,6 +38,7 @@ struct SplitArgs {
   float* part_lse;             // [B][nsplit][64] natural-log lse of each split
   uint16_t* out;               // bf16 [B][64][512] (written directly when nsplit == 1)
   float* lse;                  // [B][64]
+  uint32_t* counters;          // [B] arrival counters; non-null: the last split merges
 };
 
 struct CombineArgs {
@@ -61,5 +63,6 @@ struct GatherArgs {
 hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int fmt, int B, hipStream_t stream);
+hipError_t launch_zero(uint32_t* p, size_t n, hipStream_t stream);
 
 }  // namespace smla

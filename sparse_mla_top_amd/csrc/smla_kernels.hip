@@ -24,11 +24,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
 // Source of masked rows: reading zeros keeps every MFMA operand finite.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytesBf16];
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kPRow = 36;        // floats per P^T row in LDS (32 tokens + 4 pad)
 
 template <int FMT> struct RowFmt;
 template <> struct RowFmt<kFmtFp8> {
@@ -56,62 +60,80 @@ __device__ __forceinline__ int64_t translate(const int32_t* __restrict__ page_ta
   return (int64_t)page * kPage + (i & (kPage - 1));
 }
 
+// One direct-to-LDS load: 16 bytes per lane from `src` to LDS address
+// lds_base + 16 * lane.  Written as inline asm on purpose: the compiler treats
+// its builtin form as an LDS store that may alias every later LDS read and
+// then waits for all outstanding loads (including prefetched tiles) before
+// each read.  Completion is tracked explicitly with s_waitcnt vmcnt plus a
+// workgroup barrier before any wave reads the tile.  No "memory" clobber:
+// the asm is volatile (kept in order with barriers and other asm), and
+// leaving ordinary loads free to move lets the row addresses of a whole tile
+// be read from LDS before the first load is issued.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_base)
+      : "m0");
+}
+
 // Issue the direct-to-LDS loads of one tile (kTile rows).  Row r of the tile
-// lands at lds + r * kRow; its 16-byte chunk c comes from the row's slot, or
-// from the zero row when the slot is masked.  Wave w issues instructions
-// w, w+4, ... of the tile; the count per wave is DmaCount<FMT>::of(w).
+// lands at lds + r * kRow; its 16-byte chunk c comes from the row's address
+// (the zero row when the slot is masked; bit 0 of the address marks that).
+// Issuing wave v (0..3) takes load instructions v, v+4, ... of the tile; the
+// count per wave is DmaCount<FMT>::of(v).
 template <int FMT>
-__device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ pool,
-                                           const int64_t LDS_AS* slot_s, int tok0,
-                                           uint8_t LDS_AS* lds, int wave, int lane) {
+__device__ __forceinline__ void issue_tile(const uint64_t LDS_AS* rowaddr_s, int tok0,
+                                           uint8_t LDS_AS* lds, int v, int lane) {
   constexpr int kRow = RowFmt<FMT>::kRow;
   constexpr int kChunksRow = kRow / 16;
   constexpr int kChunks = kTile * kChunksRow;
   constexpr int kInstr = (kChunks + 63) / 64;
-  // Re-derive the lane id here so the address arithmetic below is recomputed
-  // per tile instead of being hoisted out of the tile loop (and spilled).
-  int lane_v;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(lane_v) : "v"(lane));
+  constexpr int kPerWave = (kInstr + 3) / 4;
+  // all source addresses first (one LDS round trip), then the loads
+  const void* src[kPerWave];
 #pragma unroll
-  for (int j = 0; j < kInstr; ++j) {
-    if ((j & 3) != wave) continue;
-    const int c = j * 64 + lane_v;
-    if (c < kChunks) {
-      const int r = c / kChunksRow;
-      const int off = (c - r * kChunksRow) * 16;
-      const int64_t slot = slot_s[tok0 + r];
-      const uint8_t* src = slot >= 0 ? pool + slot * kRow + off : g_zero_row + off;
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(lds + j * 64 * 16), 16, 0, 0);
-    }
+  for (int q = 0; q < kPerWave; ++q) {
+    const int c = (v + 4 * q) * 64 + lane;
+    const int cc = c < kChunks ? c : 0;
+    const int r = cc / kChunksRow;
+    const int off = (cc - r * kChunksRow) * 16;
+    src[q] = (const void*)(uintptr_t)((rowaddr_s[tok0 + r] & ~1ull) + off);
+  }
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    const int j = v + 4 * q;
+    if (j < kInstr && j * 64 + lane < kChunks)
+      dma16(src[q], (uint32_t)(uintptr_t)(lds + j * 64 * 16));
   }
 }
 
 template <int FMT> struct DmaCount {
   static constexpr int kChunks = kTile * (RowFmt<FMT>::kRow / 16);
   static constexpr int kInstr = (kChunks + 63) / 64;
-  __device__ static constexpr int of(int wave) { return (kInstr - wave + 3) / 4; }
+  // issuing wave v (0..3) takes instructions v, v+4, ...
+  __host__ __device__ static constexpr int of(int v) { return (kInstr - v + 3) / 4; }
+  // waves 0 .. kRichWaves-1 issue of(0) loads per tile, the rest of(3)
+  static constexpr int kRichWaves = (kInstr % 4 == 0) ? 4 : kInstr % 4;
 };
+static_assert(DmaCount<kFmtFp8>::of(DmaCount<kFmtFp8>::kRichWaves - 1) == DmaCount<kFmtFp8>::of(0), "");
+static_assert(DmaCount<kFmtBf16>::of(DmaCount<kFmtBf16>::kRichWaves - 1) == DmaCount<kFmtBf16>::of(0), "");
 
 // s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  // n is a multiple of a per-wave DMA count; cover 0..63.
-  switch (n) {
-#define SMLA_W(k) case k: wait_vmcnt<k>(); break;
-    SMLA_W(0) SMLA_W(1) SMLA_W(2) SMLA_W(3) SMLA_W(4) SMLA_W(5) SMLA_W(6) SMLA_W(7)
-    SMLA_W(8) SMLA_W(9) SMLA_W(10) SMLA_W(11) SMLA_W(12) SMLA_W(13) SMLA_W(14) SMLA_W(15)
-    SMLA_W(16) SMLA_W(17) SMLA_W(18) SMLA_W(19) SMLA_W(20) SMLA_W(21) SMLA_W(22) SMLA_W(23)
-    SMLA_W(24) SMLA_W(25) SMLA_W(26) SMLA_W(27) SMLA_W(28) SMLA_W(29) SMLA_W(30) SMLA_W(31)
-    SMLA_W(32) SMLA_W(33) SMLA_W(34) SMLA_W(35) SMLA_W(36) SMLA_W(37) SMLA_W(38) SMLA_W(39)
-    SMLA_W(40) SMLA_W(41) SMLA_W(42) SMLA_W(43) SMLA_W(44) SMLA_W(45) SMLA_W(46) SMLA_W(47)
-    SMLA_W(48) SMLA_W(49) SMLA_W(50) SMLA_W(51) SMLA_W(52) SMLA_W(53) SMLA_W(54) SMLA_W(55)
-    SMLA_W(56) SMLA_W(57) SMLA_W(58) SMLA_W(59) SMLA_W(60) SMLA_W(61) SMLA_W(62) SMLA_W(63)
-#undef SMLA_W
-    default: wait_vmcnt<0>(); break;
-  }
+// Wait until at most `tiles_after` tiles' worth of this wave's loads are
+// outstanding (loads complete in issue order), i.e. every earlier tile landed.
+template <int PER_TILE>
+__device__ __forceinline__ void wait_tiles(int tiles_after) {
+  static_assert(3 * PER_TILE < 64, "vmcnt range");
+  if (tiles_after >= 3) wait_vmcnt<3 * PER_TILE>();
+  else if (tiles_after == 2) wait_vmcnt<2 * PER_TILE>();
+  else if (tiles_after == 1) wait_vmcnt<PER_TILE>();
+  else wait_vmcnt<0>();
 }
 
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint64_t v) {
@@ -127,17 +149,31 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint64_t v) {
   return r;
 }
 
-__device__ __forceinline__ float wave_max16(float v) {
-  // max over lanes l, l^16, l^32, l^48 (the four row groups of an MFMA tile)
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+// Reductions over lanes l, l^16, l^32, l^48 (the four row groups of a
+// 16-wide MFMA tile) with the VALU lane-swap instructions, no LDS round trip.
+// v_permlane16_swap_b32 a, b exchanges the odd 16-lane rows of a with the even
+// rows of b; with a = b = x it leaves {x[l], x[l^16]} across the pair (a, b)
+// in every lane.  v_permlane32_swap_b32 does the same across 32-lane halves.
+// Inline asm because the builtin's lowering assumes only the first operand
+// changes; s_nop padding covers the VALU-write to permlane-read hazard.
+__device__ __forceinline__ void lane_swap16(float v, float& a, float& b) {
+  unsigned x = __builtin_bit_cast(unsigned, v), y = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
 }
-__device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+__device__ __forceinline__ void lane_swap32(float v, float& a, float& b) {
+  unsigned x = __builtin_bit_cast(unsigned, v), y = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
 }
+__device__ __forceinline__ float xor16_max(float v) { float a, b; lane_swap16(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float xor32_max(float v) { float a, b; lane_swap32(v, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float xor16_sum(float v) { float a, b; lane_swap16(v, a, b); return a + b; }
+__device__ __forceinline__ float xor32_sum(float v) { float a, b; lane_swap32(v, a, b); return a + b; }
+__device__ __forceinline__ float wave_max16(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float wave_sum16(float v) { return xor32_sum(xor16_sum(v)); }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() would also wait for
 // every outstanding global load, including the prefetched tiles in flight.
@@ -162,226 +198,500 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 }
 
 // ----------------------------------------------------------------------------
-// Split kernel.  256 threads = 4 waves; wave w owns heads 16w..16w+15 of the
-// request and walks all tiles of the workgroup's top-k chunk.
+// Log-sum-exp merge of the nsplit partials of request b by one 512-thread
+// workgroup: out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
+// M = max_s lse_s, lse = M + ln sum_s w_s; all splits empty -> out 0, lse -inf.
+// Thread t owns head t/8 and dims 64(t%8) .. +63.
+__device__ __forceinline__ void merge_request(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                              int nsplit, int b, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int h = threadIdx.x >> 3, d0 = 64 * (threadIdx.x & 7);
+  const float* ls = part_lse + (int64_t)b * nsplit * kHeads + h;
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ls[sp * kHeads]);
+  float acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float l = ls[sp * kHeads];
+      if (l == -INFINITY) continue;
+      const float wgt = __expf(l - M);
+      wsum += wgt;
+      const float4* src = reinterpret_cast<const float4*>(part_o + (((int64_t)b * nsplit + sp) * kHeads + h) * kDv + d0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 v = src[i];
+        acc[4 * i] += wgt * v.x; acc[4 * i + 1] += wgt * v.y; acc[4 * i + 2] += wgt * v.z; acc[4 * i + 3] += wgt * v.w;
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  uint16_t* orow = out + ((int64_t)b * kHeads + h) * kDv + d0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint4 w4;
+    w4.x = (uint32_t)f32_to_bf16_rne(acc[8 * i] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 1] * inv) << 16);
+    w4.y = (uint32_t)f32_to_bf16_rne(acc[8 * i + 2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 3] * inv) << 16);
+    w4.z = (uint32_t)f32_to_bf16_rne(acc[8 * i + 4] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 5] * inv) << 16);
+    w4.w = (uint32_t)f32_to_bf16_rne(acc[8 * i + 6] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 7] * inv) << 16);
+    *reinterpret_cast<uint4*>(orow + 8 * i) = w4;
+  }
+  if ((threadIdx.x & 7) == 0) lse[(int64_t)b * kHeads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+}
+
+// ----------------------------------------------------------------------------
+// Split kernel.  512 threads// ----------------------------------------------------------------------------
+// Split kernel.  512 threads = 8 waves, one workgroup per (request, split),
+// with two roles that run side by side on each SIMD (waves w and w+4 share
+// SIMD w):
 //
-// Per 32-token tile, per wave:
-//   S^T[32 tok][16 heads] = K[32][576] . Q^T   (2 x 18 MFMA 16x16x32 bf16)
-//     K operand: lane (token l%16, group g) holds dims 32c+8g..+7 of its row,
-//     fp8 codes converted exactly to bf16; fp8 block scales multiply the fp32
-//     partial of each 128-dim block.
-//   online softmax in the log2 domain, per head (lane column l%16).
-//   O^T[512 d][16 heads] += V^T[512][32 tok] . P^T   (32 MFMA 16x16x32 bf16)
-//     V^T operand: one ds_read_tr8_b64 (fp8) / two ds_read_tr16_b64 (bf16)
-//     gives lane (d l%16, group g) the 8 tokens of its k-slots; fp8 block
-//     scales are folded into P (one bf16 P operand per 128-dim block).
-// k-slot i of lane group g maps to token tok(g,i) = (i<4) ? 4g+i : 16+4g+i-4,
-// which is exactly where the S^T accumulators of the two 16-token halves hold
-// them, so P never leaves registers.
+//   QK waves 0..3 own heads 16w..16w+15 and every score dim:
+//     S^T[16 tok][16 heads] per 16-token half of a 32-token tile.
+//     fp8 rows: per 128-dim scale block one 16x16x128 fp8 MFMA on the cache
+//     codes as stored, against Q split exactly into fp8 hi + lo parts
+//     (Q * 2^e_h = hi + lo, e_h a per-head power of two); the block scale
+//     multiplies the fp32 block partial; the 64 rope dims use 16x16x32 bf16
+//     MFMA.  bf16 rows: 18 bf16 MFMA.  In both operands k-slot g of a block
+//     covers dims 32g..32g+31, so the products pair the same dims.
+//     Online softmax in the log2 domain per head (lane column); the running
+//     max is only raised when a tile's max exceeds it by more than 2^8, so
+//     the output is rarely rescaled (p stays <= 2^8).  P^T goes to LDS, one
+//     bf16 copy per scale block with that block's scales folded in.
+//   PV waves 4..7 own latent dims 128v..128v+127 (scale block v = w-4) for
+//     all 64 heads: O^T[16 d][16 heads] += V^T[16 d][32 tok] . P^T[32 tok][16 h]
+//     with V^T from one ds_read_tr8_b64 (fp8, converted exactly to bf16) or
+//     two ds_read_tr16_b64 (bf16) per 16-dim tile.
+//
+// Iteration k of the shared loop: QK waves score tile k while PV waves
+// accumulate tile k-1; one workgroup barrier per iteration.  Rows stream into a
+// ring of kNbuf LDS tile buffers with direct-to-LDS loads issued ahead.
+// k-slot i of lane group g holds token tok(g,i) = (i<4) ? 4g+i : 16+4g+i-4,
+// which is where the S^T accumulators of the two halves hold them.
 template <int FMT>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   constexpr int kRow = RowFmt<FMT>::kRow;
   constexpr int kNbuf = RowFmt<FMT>::kNbuf;
   constexpr int kTileBytes = kTile * kRow;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kNbuf * kTileBytes];
-  __shared__ int64_t slot_s[kTopk];
+  __shared__ uint64_t rowaddr_s[kTopk];            // row address | 1 when masked
+  __shared__ uint32_t mask_s[kTiles];              // bit t: token t of the tile is valid
+  // P^T (fp32, unscaled) in [head][token] rows padded to 36 floats so the
+  // 16-byte accesses of 8 consecutive lanes hit distinct banks
+  __shared__ __attribute__((aligned(16))) float p_s[2][kHeads][kPRow];
+  __shared__ float alpha_s[2][kHeads];
+  __shared__ float fin_s[kHeads];
+  __shared__ int last_s;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4;          // row group of MFMA layouts
   const int c16 = lane & 15;        // column within a 16-wide MFMA tile
+  const bool qk_role = wave < 4;
 
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int b = w / a.nsplit;
   const int s = w - b * a.nsplit;
   const int tile0 = s * a.chunk_tiles;
-  if (tile0 >= kTopk / kTile) return;   // empty split (host never launches one)
-  const int ntiles = min(a.chunk_tiles, kTopk / kTile - tile0);
+  if (tile0 >= kTiles) return;   // empty split (the host never launches one)
+  const int ntiles = min(a.chunk_tiles, kTiles - tile0);
   const int ntok = ntiles * kTile;
   const int ctx = a.ctx_len[b];
 
-  // 1. index translation for the whole chunk
-  for (int t = threadIdx.x; t < ntok; t += kThreads)
-    slot_s[t] = translate(a.page_table, a.topk_idx, ctx, b, tile0 * kTile + t, a.max_pages,
-                          a.pool_pages);
-
-  // 2. Q^T fragment of this wave's 16 heads: 18 chunks of 32 dims, 8 per lane
-  const int head = wave * 16 + c16;
+  // ---- 1. QK waves: raw Q of their 16 heads (lane column = head)
+  const int head = (wave & 3) * 16 + c16;
   const uint16_t* qrow = a.q + ((int64_t)b * kHeads + head) * kDqk;
-  bf16x8 qf[18];
+  bf16x8 qraw[18];
+  if (qk_role) {
+    if constexpr (FMT == kFmtFp8) {
+      // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
 #pragma unroll
-  for (int c = 0; c < 18; ++c)
-    qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qraw[4 * blk + j] = *reinterpret_cast<const bf16x8*>(qrow + 128 * blk + 32 * g + 8 * j);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+    }
+#pragma unroll
+    for (int c = 16; c < 18; ++c)
+      qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+  }
 
+  // ---- 2. index translation, one token per thread (its latency overlaps Q's)
+  {
+    const int t = threadIdx.x;
+    bool valid = false;
+    if (t < ntok) {
+      const int64_t slot = translate(a.page_table, a.topk_idx, ctx, b, tile0 * kTile + t, a.max_pages,
+                                     a.pool_pages);
+      valid = slot >= 0;
+      rowaddr_s[t] = valid ? (uint64_t)(uintptr_t)(a.pool + slot * kRow)
+                           : ((uint64_t)(uintptr_t)g_zero_row | 1ull);
+    }
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(valid);
+    if (lane == 0 && 2 * wave < kTiles) {
+      mask_s[2 * wave] = (uint32_t)bits;
+      mask_s[2 * wave + 1] = (uint32_t)(bits >> 32);
+    }
+  }
+  // Q must have landed before the first tile load is issued: the tile loads
+  // are invisible to the compiler's wait counting, so any wait it placed for
+  // Q later on would also drain every prefetched tile.
+  if (qk_role) {
+#pragma unroll
+    for (int c = 0; c < 18; ++c) asm volatile("" : "+v"(qraw[c]));
+  }
   lds_barrier();
 
-  // 3. prefetch the first tiles
-  const int npre = min(kNbuf, ntiles);
-  for (int tt = 0; tt < npre; ++tt)
-    issue_tile<FMT>(a.pool, (const int64_t LDS_AS*)slot_s, tt * kTile,
-                    (uint8_t LDS_AS*)(tiles + tt * kTileBytes), wave, lane);
+  // ---- 3. the PV waves issue every tile load (the QK waves never wait on
+  // the texture path); first the prefetch of the first kNbuf tiles
+  const int vwave = wave & 3;
+  // kAhead tiles are in flight beyond the one being scored: tile k + kAhead is
+  // issued at iteration k into the buffer of tile k - 2 (scored at k - 2,
+  // accumulated at k - 1, so free after the barrier of iteration k).
+  constexpr int kAhead = kNbuf - 2;
+  const int npre = min(kAhead, ntiles);
+  if (!qk_role)
+    for (int tt = 0; tt < npre; ++tt)
+      issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile,
+                      (uint8_t LDS_AS*)(tiles + tt * kTileBytes), vwave, lane);
 
-  const int dma_per_tile = DmaCount<FMT>::of(wave);
-
-  f32x4 o[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max (log2 domain), per head = lane column
-  float l_run = 0.f;         // this lane's share of the running sum
-
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int issued = min(ntiles, kNbuf + tt);
-    wait_vmcnt_rt((issued - tt - 1) * dma_per_tile);
+  // Top of iteration k: the PV waves wait for their share of tile k, then a
+  // barrier publishes it; then they issue tile k + kAhead.
+  auto iteration_head = [&](int k) {
+    if (!qk_role && k < ntiles) {
+      const int after = min(ntiles, k + kAhead) - k - 1;   // tiles issued after tile k
+      if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(after);
+      else wait_tiles<DmaCount<FMT>::of(3)>(after);
+    }
     lds_barrier();
+    if (!qk_role && k + kAhead < ntiles)
+      issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, (k + kAhead) * kTile,
+                      (uint8_t LDS_AS*)(tiles + ((k + kAhead) % kNbuf) * kTileBytes), vwave, lane);
+  };
 
-    const uint8_t* tb = tiles + (tt % kNbuf) * kTileBytes;
-    const int tok_base = tt * kTile;
-
-    // ---- scores S^T for the two 16-token halves
-    f32x4 sacc[2];
+  if (qk_role) {
+    // ---------------------------------------------------------------- QK role
+    i32x8 qhi[FMT == kFmtFp8 ? 4 : 1], qlo[FMT == kFmtFp8 ? 4 : 1];
+    bf16x8 qb[18];
+    float qscale = 1.0f;           // 2^-e_h, folded into the softmax scale
+    if constexpr (FMT == kFmtFp8) {
+      float amax = 0.f;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const uint8_t* krow = tb + (16 * m + c16) * kRow;
-      f32x4 sm = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (FMT == kFmtFp8) {
-        float4 scl[4];     // block scales of tokens 16m + 4g + i
+      for (int c = 0; c < 16; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          scl[i] = *reinterpret_cast<const float4*>(tb + (16 * m + 4 * g + i) * kRow + kDl);
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)qraw[c][e]));
+      amax = wave_max16(amax);
+      // e_h: largest power of two with amax * 2^e_h <= 448 (the e4m3 maximum)
+      int ex = 0;
+      if (amax > 0.f) {
+        const int E = __builtin_amdgcn_frexp_expf(amax);          // amax = m * 2^E, m in [0.5,1)
+        const float mnt = __builtin_amdgcn_frexp_mantf(amax);
+        ex = (mnt <= 0.875f) ? 9 - E : 8 - E;
+        ex = max(-120, min(120, ex));
+      }
+      const float up = __builtin_ldexpf(1.0f, ex);
+      qscale = __builtin_ldexpf(1.0f, -ex);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const int c = blk * 4 + c4;
-            const uint64_t raw = *reinterpret_cast<const uint64_t*>(krow + 32 * c + 8 * g);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(raw), qf[c], acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            float x[4], hf[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (float)qraw[4 * blk + j][4 * h2 + e] * up;
+            int hv = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+            hv = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], hv, true);
+            hf[0] = __builtin_amdgcn_cvt_f32_fp8(hv, 0);
+            hf[1] = __builtin_amdgcn_cvt_f32_fp8(hv, 1);
+            hf[2] = __builtin_amdgcn_cvt_f32_fp8(hv, 2);
+            hf[3] = __builtin_amdgcn_cvt_f32_fp8(hv, 3);
+            int lv = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] - hf[0], x[1] - hf[1], 0, false);
+            lv = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - hf[2], x[3] - hf[3], lv, true);
+            qhi[blk][2 * j + h2] = hv;
+            qlo[blk][2 * j + h2] = lv;
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sm[i] += acc[i] * (&scl[i].x)[blk];
-        }
+      for (int c = 16; c < 18; ++c)
 #pragma unroll
-        for (int c = 16; c < 18; ++c) {
-          const bf16x8 kr = *reinterpret_cast<const bf16x8*>(krow + kDl + 16 + 2 * (32 * (c - 16) + 8 * g));
-          sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, qf[c], sm, 0, 0, 0);
-        }
-      } else {
+        for (int e = 0; e < 8; ++e) qb[c][e] = (__bf16)((float)qraw[c][e] * up);   // exact: power of two
+    } else {
 #pragma unroll
-        for (int c = 0; c < 18; ++c) {
-          const bf16x8 kr = *reinterpret_cast<const bf16x8*>(krow + 2 * (32 * c + 8 * g));
-          sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr, qf[c], sm, 0, 0, 0);
+      for (int c = 0; c < 18; ++c) qb[c] = qraw[c];
+    }
+    const float sc_log2 = a.scale_log2 * qscale;
+    float m_run = -INFINITY;        // running max (log2 domain) of this lane's head
+    float l_run = 0.f;              // this lane's share of the running sum
+
+    // Iteration k = -1 is a warm-up pass through the same loop code on
+    // whatever buffer 0 holds, with every slot masked and its state thrown
+    // away: it pulls the loop's instructions into the instruction cache while
+    // the first tile is still in flight.  Its P/alpha writes land in buffer 0,
+    // which the real iteration 0 overwrites before any PV wave reads it.
+    const int kfirst = __builtin_amdgcn_readfirstlane(a.nsplit > 0 ? -1 : 0);
+#pragma clang loop unroll(disable)
+    for (int k = kfirst; k <= ntiles; ++k) {
+      const bool dry = k < 0;
+      if (!dry) iteration_head(k);
+      if (k == ntiles) break;
+      const int kt = dry ? 0 : k;
+      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+      const uint32_t vmask = dry ? 0u : mask_s[kt];
+
+      // all operand reads of both 16-token halves first
+      i32x8 ka[2][4];
+      bf16x8 kr[2][18];
+      float4 sv[2][4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint8_t* krow = tb + (16 * m + c16) * kRow;
+        if constexpr (FMT == kFmtFp8) {
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            const i32x4 k0 = *reinterpret_cast<const i32x4*>(krow + 128 * blk + 32 * g);
+            const i32x4 k1 = *reinterpret_cast<const i32x4*>(krow + 128 * blk + 32 * g + 16);
+            ka[m][blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            kr[m][16 + c] = *reinterpret_cast<const bf16x8*>(krow + kDl + 16 + 2 * (32 * c + 8 * g));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sv[m][i] = *reinterpret_cast<const float4*>(tb + (16 * m + 4 * g + i) * kRow + kDl);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 18; ++c)
+            kr[m][c] = *reinterpret_cast<const bf16x8*>(krow + 2 * (32 * c + 8 * g));
         }
       }
-      sacc[m] = sm;
-    }
 
-    // ---- online softmax (log2 domain); masked slots score -inf
-    float p[8];
-    float tmax = -INFINITY;
+      // scores S^T for the two 16-token halves: independent MFMA chains
+      // (hi of every block, rope, then lo), block scales last
+      f32x4 sacc[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m) {
+        f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FMT == kFmtFp8) {
+          f32x4 acc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tok_base + 16 * m + 4 * g + i;
-        const float v = slot_s[t] >= 0 ? sacc[m][i] * a.scale_log2 : -INFINITY;
-        p[4 * m + i] = v;
-        tmax = fmaxf(tmax, v);
+          for (int blk = 0; blk < 4; ++blk)
+            acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qhi[blk], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                       0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m][16 + c], qb[16 + c], sm, 0, 0, 0);
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+            acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qlo[blk], acc[blk], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm[i] += acc[blk][i] * (&sv[m][i].x)[blk];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 18; ++c)
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m][c], qb[c], sm, 0, 0, 0);
+        }
+        sacc[m] = sm;
       }
-    tmax = wave_max16(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);   // 0 while nothing seen, 1 if max unchanged
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(p[i] - m_use);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-    }
 
-    // ---- P^T operands (fp8: one per 128-dim block with its scales folded in)
-    constexpr int kNP = (FMT == kFmtFp8) ? 4 : 1;
-    bf16x8 pb[kNP];
-    if constexpr (FMT == kFmtFp8) {
+      // online softmax (log2 domain); masked slots score -inf
+      float p[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = (vmask >> (16 * m + 4 * g + i)) & 1u;
+          const float v = ok ? sacc[m][i] * sc_log2 : -INFINITY;
+          p[4 * m + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = wave_max16(tmax);
+      float m_cur = dry ? -INFINITY : m_run;
+      float alpha = 1.0f;
+      if (__builtin_amdgcn_ballot_w64(tmax > m_cur + 8.0f)) {
+        const float m_new = (tmax > m_cur + 8.0f) ? tmax : m_cur;
+        alpha = __builtin_amdgcn_exp2f(m_cur - m_new);   // 0 when nothing was seen before
+        m_cur = m_new;
+      }
+      const float m_use = (m_cur == -INFINITY) ? 0.f : m_cur;
+      float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float4 sv = *reinterpret_cast<const float4*>(
-            tb + (16 * (i >> 2) + 4 * g + (i & 3)) * kRow + kDl);
-        pb[0][i] = (__bf16)(p[i] * sv.x);
-        pb[1][i] = (__bf16)(p[i] * sv.y);
-        pb[2][i] = (__bf16)(p[i] * sv.z);
-        pb[3][i] = (__bf16)(p[i] * sv.w);
+        p[i] = __builtin_amdgcn_exp2f(p[i] - m_use);
+        psum += p[i];
+      }
+      if (!dry) {
+        m_run = m_cur;
+        l_run = l_run * alpha + psum;
+      }
+
+      // P^T rows (fp32, unscaled) for the PV waves; this lane holds tokens
+      // 16m + 4g .. +3 of its head
+      const int pb = kt & 1;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        *reinterpret_cast<float4*>(&p_s[pb][head][16 * m + 4 * g]) =
+            make_float4(p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]);
+      if (g == 0) alpha_s[pb][head] = alpha;
+    }
+
+    // normaliser of each head for the PV waves; lse from here
+    const float L = wave_sum16(l_run);
+    if (g == 0) {
+      fin_s[head] = L;
+      const float lse_v = L > 0.f ? (m_run + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+      if (a.nsplit == 1) a.lse[(int64_t)b * kHeads + head] = lse_v;
+      else a.part_lse[((int64_t)b * a.nsplit + s) * kHeads + head] = lse_v;
+    }
+    lds_barrier();
+  } else {
+    // ---------------------------------------------------------------- PV role
+    // 32x32x16 bf16 MFMA: O^T[32 d][32 heads] += V^T[32 d][16 tok] . P^T[16 tok][32 heads].
+    // Operand lane layout (both): row/col = lane % 32, k = 8 * (lane / 32) + i,
+    // so k-slot (lane/32, i) of k-half kh is token 16kh + 8(lane/32) + i.
+    const int vb = wave - 4;          // scale block / 128-dim slice of the latent
+    const int l32 = lane & 31, kg = lane >> 5;
+    f32x16 o[4][2];                   // [32-dim block of the slice][32-head block]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
+
+    // Iteration 0 has no P yet: it is a warm-up pass through the same loop
+    // code on tile 0 and an unwritten P buffer (loading the instructions into
+    // the cache while the QK waves score tile 0); its accumulators are reset.
+#pragma clang loop unroll(disable)
+    for (int k = 0; k <= ntiles; ++k) {
+      iteration_head(k);
+      const bool dry = k == 0;
+      const int kt = dry ? 0 : k - 1;   // tile accumulated in this iteration
+      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+      const int pb = dry ? 1 : kt & 1;
+      // P^T operands [head block][k-half]: 8 tokens 16kh + 8kg + i of head
+      // 32hb + l32, times this slice's block scale for fp8 rows, in bf16
+      bf16x8 pv[2][2];
+      float al[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        float sc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          sc[i] = (FMT == kFmtFp8) ? *reinterpret_cast<const float*>(tb + (16 * kh + 8 * kg + i) * kRow + kDl + 4 * vb)
+                                   : 1.0f;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const float4 p0 = *reinterpret_cast<const float4*>(&p_s[pb][32 * hb + l32][16 * kh + 8 * kg]);
+          const float4 p1 = *reinterpret_cast<const float4*>(&p_s[pb][32 * hb + l32][16 * kh + 8 * kg + 4]);
+          bf16x8 v;
+          v[0] = (__bf16)(p0.x * sc[0]); v[1] = (__bf16)(p0.y * sc[1]);
+          v[2] = (__bf16)(p0.z * sc[2]); v[3] = (__bf16)(p0.w * sc[3]);
+          v[4] = (__bf16)(p1.x * sc[4]); v[5] = (__bf16)(p1.y * sc[5]);
+          v[6] = (__bf16)(p1.z * sc[6]); v[7] = (__bf16)(p1.w * sc[7]);
+          pv[hb][kh] = v;
+        }
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) al[hb] = alpha_s[pb][32 * hb + l32];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        if (__builtin_amdgcn_ballot_w64(al[hb] != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[db][hb] *= al[hb];
+        }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          bf16x8 va;
+          if constexpr (FMT == kFmtFp8) {
+            // 16-lane group gg reads tokens 16kh + 8(gg>>1) + 0..7 x dims
+            // 32db + 16(gg&1) + 0..15; source lane (2r + half) supplies 8 bytes of row r
+            const int gg = lane >> 4, r = c16 >> 1, half = c16 & 1;
+            const uint8_t* src = tb + (16 * kh + 8 * (gg >> 1) + r) * kRow + 128 * vb + 32 * db + 16 * (gg & 1) + 8 * half;
+            const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
+            va = fp8x8_to_bf16((uint64_t)(uint32_t)raw[0] | ((uint64_t)(uint32_t)raw[1] << 32));
+          } else {
+            // two 4-row reads per group: rows 16kh + 8(gg>>1) + 0..3 and + 4..7;
+            // source lane (4r + q) supplies 4 elements of row r
+            const int gg = lane >> 4, r = c16 >> 2, q = c16 & 3;
+            const uint8_t* src = tb + (16 * kh + 8 * (gg >> 1) + r) * kRow + 2 * (128 * vb + 32 * db + 16 * (gg & 1)) + 8 * q;
+            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)src);
+            const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(src + 4 * kRow));
+            // whole-vector bit casts: element-wise short -> __bf16 casts of this
+            // result were mis-lowered (the upper dword was dropped)
+            const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
+            const i32x2 a1 = __builtin_bit_cast(i32x2, r1);
+            const i32x4 packed = {a0[0], a0[1], a1[0], a1[1]};
+            va = __builtin_bit_cast(bf16x8, packed);
+          }
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[hb][kh], o[db][hb], 0, 0, 0);
+        }
+      if (dry) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
+      }
+    }
+
+    lds_barrier();                    // QK waves have published the normalisers
+    float inv[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float Lh = fin_s[32 * hb + l32];
+      inv[hb] = Lh > 0.f ? 1.0f / Lh : 0.f;
+    }
+    // register j of o[db][hb] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head = 32hb + l32]
+    if (a.nsplit == 1) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        uint16_t* orow = a.out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 4 * kg;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float v0 = o[db][hb][4 * jj], v1 = o[db][hb][4 * jj + 1];
+            const float v2 = o[db][hb][4 * jj + 2], v3 = o[db][hb][4 * jj + 3];
+            const uint32_t lo = (uint32_t)f32_to_bf16_rne(v0 * inv[hb]) | ((uint32_t)f32_to_bf16_rne(v1 * inv[hb]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_rne(v2 * inv[hb]) | ((uint32_t)f32_to_bf16_rne(v3 * inv[hb]) << 16);
+            *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
+          }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[0][i] = (__bf16)p[i];
-    }
-
-    // ---- O^T += V^T P^T over the 32 d-tiles
-    if constexpr (FMT == kFmtFp8) {
-      // source lane (2k + half) of a group supplies 8 bytes of token tok(g,k)
-      const int kk = c16 >> 1, half = c16 & 1;
-      const int tok = (kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4);
-      const uint8_t* vsrc = tb + tok * kRow + 8 * half;
+      for (int hb = 0; hb < 2; ++hb) {
+        float* prow = a.part_o + (((int64_t)b * a.nsplit + s) * kHeads + 32 * hb + l32) * kDv + 128 * vb + 4 * kg;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)(vsrc + 16 * dt));
-        const uint64_t r64 = (uint64_t)(uint32_t)raw[0] | ((uint64_t)(uint32_t)raw[1] << 32);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(r64), pb[dt >> 3], o[dt], 0, 0, 0);
-      }
-    } else {
-      // source lane (4k + q) of a group supplies 4 elements of token tok(g,k) / tok(g,4+k)
-      const int kk = c16 >> 2, qd = c16 & 3;
-      const uint8_t* v0 = tb + (4 * g + kk) * kRow + 8 * qd;
-      const uint8_t* v1 = tb + (16 + 4 * g + kk) * kRow + 8 * qd;
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(v0 + 32 * dt));
-        const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(v1 + 32 * dt));
-        // whole-vector bit casts: element-wise short -> __bf16 casts of this
-        // result were mis-lowered (the upper dword was dropped)
-        const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
-        const i32x2 a1 = __builtin_bit_cast(i32x2, r1);
-        const i32x4 packed = {a0[0], a0[1], a1[0], a1[1]};
-        const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[0], o[dt], 0, 0, 0);
+          for (int jj = 0; jj < 4; ++jj) {
+            *reinterpret_cast<float4*>(prow + 32 * db + 8 * jj) =
+                make_float4(o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb],
+                            o[db][hb][4 * jj + 2] * inv[hb], o[db][hb][4 * jj + 3] * inv[hb]);
+          }
       }
-    }
-
-    // ---- refill this buffer with tile tt + kNbuf
-    if (tt + kNbuf < ntiles) {
-      lds_barrier();
-      issue_tile<FMT>(a.pool, (const int64_t LDS_AS*)slot_s, (tt + kNbuf) * kTile,
-                      (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), wave, lane);
     }
   }
 
-  // ---- finish: normalise and write
-  const float L = wave_sum16(l_run);
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const float lse_v = L > 0.f ? (m_run + log2f(L)) * kLn2 : -INFINITY;
-  // lane holds O^T[d = 16dt + 4g + i][head]
-  if (a.nsplit == 1) {
-    uint16_t* orow = a.out + ((int64_t)b * kHeads + head) * kDv;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[dt][1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo, hi);
+  // ---- fused combine: the last split of a request to finish merges them
+  if (a.nsplit > 1 && a.counters != nullptr) {
+    __threadfence();                     // this workgroup's partials, device-visible
+    lds_barrier();
+    if (threadIdx.x == 0) last_s = atomicAdd(&a.counters[b], 1u) == (uint32_t)(a.nsplit - 1);
+    lds_barrier();
+    if (last_s) {
+      __threadfence();                   // acquire the other splits' partials
+      merge_request(a.part_o, a.part_lse, a.nsplit, b, a.out, a.lse);
+      if (threadIdx.x == 0) a.counters[b] = 0u;   // ready for the next call
     }
-    if (g == 0) a.lse[(int64_t)b * kHeads + head] = lse_v;
-  } else {
-    float* prow = a.part_o + (((int64_t)b * a.nsplit + s) * kHeads + head) * kDv;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      *reinterpret_cast<float4*>(prow + 16 * dt + 4 * g) =
-          make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-    if (g == 0) a.part_lse[((int64_t)b * a.nsplit + s) * kHeads + head] = lse_v;
   }
 }
 
@@ -432,6 +742,14 @@ __global__ __launch_bounds__(64) void gather_kernel(GatherArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Fill kernel that zeroes a counter array (used instead of a memset so that a
+// captured graph holds only kernel nodes).
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ----------------------------------------------------------------------------
 // Launchers (host side).
 hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t stream) {
   if (fmt == kFmtFp8)
@@ -443,6 +761,12 @@ hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t st
 
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream) {
   hipLaunchKernelGGL(combine_kernel, dim3(B * kHeads), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(uint32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

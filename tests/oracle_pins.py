@@ -46,9 +46,10 @@ def _valid_rows(w: W.Workload, pool: np.ndarray, b: int) -> np.ndarray:
     rb = w.row_bytes
     out = []
     for i in w.topk_idx[b]:
-        if 0 <= i < w.ctx_len[b]:
-            page = int(w.page_table[b, i // W.PAGE])
-            out.append(pool[(page * W.PAGE + i % W.PAGE) * rb:(page * W.PAGE + i % W.PAGE + 1) * rb])
+        i = int(i)
+        if 0 <= i < int(w.ctx_len[b]):
+            slot = int(w.page_table[b, i // W.PAGE]) * W.PAGE + i % W.PAGE
+            out.append(pool[slot * rb:(slot + 1) * rb])
     return np.array(out, dtype=np.uint8).reshape(len(out), rb)
 
 

@@ -10,6 +10,9 @@ lse = -inf.
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 TOL = 6.7e-3
@@ -35,6 +38,10 @@ def compare(out, lse, ref_o, ref_l):
 def assert_parity(out, lse, ref_o, ref_l, what=""):
     rel, dl, n = compare(out, lse, ref_o, ref_l)
     print(f"[parity] {what}: rows={n} max_rel={rel:.3e} max_dlse={dl:.3e}", flush=True)
+    log = os.environ.get("SMLA_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": what, "rows": n, "max_rel": rel, "max_dlse": dl}) + "\n")
     assert rel <= TOL, f"{what}: relative error {rel:.3e} > {TOL}"
     assert dl <= TOL, f"{what}: lse error {dl:.3e} > {TOL}"
     return rel, dl

@@ -86,8 +86,9 @@ def test_forced_nsplit_normalised_to_whole_tiles(forced, expect):
     assert p.nsplit == expect
     chunk = math.ceil(16 / p.nsplit)
     assert (p.nsplit - 1) * chunk < 16 <= p.nsplit * chunk
-    assert ws == (0 if expect == 1 else (((8 * expect * 64 * 512 * 4) + 255) // 256 * 256
-                                         + ((8 * expect * 64 * 4) + 255) // 256 * 256))
+    a256 = lambda x: (x + 255) // 256 * 256
+    # partial outputs, partial lse, one arrival counter per request
+    assert ws == (0 if expect == 1 else a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4) + a256(8 * 4))
 
 
 def test_selector_is_shape_only_and_bounded():

@@ -178,7 +178,7 @@ def test_split_and_combine_stages_equal_decode():
     shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages)
     for ns in (1, 4):
         plan, ws_bytes = smla.plan_for(shape, ns)
-        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+        ws = smla.new_workspace(ws_bytes)
         o1 = torch.empty((w.B, 64, 512), dtype=torch.bfloat16, device="cuda")
         l1 = torch.empty((w.B, 64), dtype=torch.float32, device="cuda")
         o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
@@ -187,3 +187,32 @@ def test_split_and_combine_stages_equal_decode():
         assert smla.combine_raw(shape, ns, ws, o2, l2) == 0
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fused_merge_repeated_calls_share_workspace():
+    """One workspace reused across calls, plans and batch sizes: the arrival
+    counters must come back to zero after every call."""
+    ws = smla.new_workspace(80 << 20)
+    for it, (wid, ns) in enumerate([(2, 4), (2, 4), (3, 3), (2, 16), (4, 6), (2, 4)]):
+        w = W.make(wid)
+        pool = w.host_pool()
+        d = upload(w)
+        out, lse = smla.decode(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, kv_format=d.kv_format,
+                               pool_pages=d.pool_pages, plan=ns, workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.decode_workload(w, pool=pool)
+        assert_parity(out, lse, ref_o, ref_l, f"fused merge call {it} {w.name} nsplit={ns}")
+
+
+def test_workspace_init_recovers_dirty_counters():
+    w = W.make(2)
+    d = upload(w)
+    shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages)
+    plan, ws_bytes = smla.plan_for(shape, 4)
+    ws = torch.full((ws_bytes,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage everywhere
+    smla.workspace_init(ws)
+    out, lse = smla.decode(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, kv_format=d.kv_format,
+                           pool_pages=d.pool_pages, plan=4, workspace=ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode_workload(w)
+    assert_parity(out, lse, ref_o, ref_l, "after workspace_init")
