@@ -1,18 +1,28 @@
 #!/usr/bin/env python
 """Benchmark of the sparse-MLA decode hot path on one MI355X.
 
-One step = one decode call (split kernel + combine kernel) over one layer's
-batch.  The headline workload is B = 80 requests x 64 heads, top-k 512 over a
-131072-token context per request, fp8 cache rows, 70/30 recent/older index mix.
-`--sets` independent seeded input sets (own Q, indices, page table and rows, in
-disjoint regions of one device pool) are cycled so that successive calls gather
-cold rows: 16 sets touch ~640 MB, more than the 256 MB Infinity Cache.
+One step = one `sparse_mla_decode` call over one layer's batch: index
+translation, gather, QK^T, online softmax, PV, split-K partials and their LSE
+merge, all in one launch of the split kernel (the last split of each request
+to finish merges that request).
+
+Headline workload: B = 80 requests x 64 heads, top-k 512 over a 131072-token
+context per request, fp8 e4m3 latent rows with per-128-dim block scales and
+bf16 rope, 70/30 recent/older index mix.  `--sets` independent seeded input
+sets (own Q, indices, page table and rows, each in its own region of one
+device pool) are cycled so successive calls gather cold rows: 16 sets touch
+~640 MB, more than the 256 MB Infinity Cache.
+
+A second, shorter pass times the 512K-context uniform-index workload at
+B in {1, 8, 16, 32, 48, 64, 80, 88, 96} (cycling `--sweep-layers` layers) and
+reports per-layer us, the 42-layer step total and the per-request slope.
 
 Prints ONE JSON line.  Timing uses HIP events on the launch stream.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -27,42 +37,62 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-MLA decode µs/layer + achieved HBM GB/s (% roofline) at B=1..96"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, vendor figure
+KERNEL_NAME = "split_kernel<1>"  # fp8 instantiation: the only kernel of a call
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_fp8_b80_ctx128k_traffic.json")
+SWEEP_B = (1, 8, 16, 32, 48, 64, 80, 88, 96)
+LAYERS_PER_STEP = 42
 
 
-def algorithmic(w, split_only: bool, nsplit: int):
-    """(bytes, flops) the method must move / compute for workload w.
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("smla_kernels.hip", "smla_internal.h"):
+        with open(os.path.join(ROOT, "sparse_mla_top_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
-    Bytes: valid rows, distinct page-table entries, the top-k list, ctx_len and Q
-    are read; out (bf16) and lse (fp32) are written.  When the call is split the
-    split kernel does not write out/lse (the combine kernel does).
+
+def algorithmic(w):
+    """(bytes, flops) one call must move / compute for workload w.
+
+    Bytes read: every valid selected row (656 B fp8 / 1152 B bf16), the
+    distinct page-table entries it needs, the top-k list, ctx_len and Q
+    (64 x 576 bf16 per request).  Bytes written: out (64 x 512 bf16) and lse
+    (64 fp32) per request.  Split-K partials are not counted: they are this
+    implementation's overhead, not the method's.
+    Flops: per valid (request, head, row) 2*576 for QK^T and 2*512 for PV.
     """
     i = w.topk_idx.astype(np.int64)
     valid = (i >= 0) & (i < w.ctx_len[:, None])
-    n_valid = valid.sum()
+    n_valid = int(valid.sum())
     pages = sum(len(np.unique(i[b][valid[b]] // 64)) for b in range(w.B))
     B = w.B
     rd = n_valid * w.row_bytes + 4 * pages + 4 * 512 * B + 4 * B + B * 64 * 576 * 2
     wr = B * 64 * 512 * 2 + B * 64 * 4
-    byts = rd + (0 if (split_only and nsplit > 1) else wr)
     flops = n_valid * 64 * (2 * 576 + 2 * 512)
-    return int(byts), int(flops)
+    return int(rd + wr), int(flops)
 
 
 def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--sets", type=int, default=16)
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--nsplit", type=int, default=0, help="force the split count (0 = selector)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the B = 1..96 pass")
+    ap.add_argument("--sweep-layers", type=int, default=4)
+    ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "this implementation runs on one GPU; multi-GPU runs are not supported "
+                                   "(--gpus must be 1)", "n_gpus": args.gpus}), flush=True)
         return 2
 
     import torch
@@ -72,45 +102,47 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+        del x, y
+
+    # ------------------------------------------------------------------ headline
     L = args.sets
     t0 = time.time()
-    sets = []
-    per_set_pages = None
-    pool = None
+    sets, pool, per_set_pages = [], None, None
     for l in range(L):
         w = W.make(3, layer=l, page_base=0 if per_set_pages is None else l * per_set_pages)
         if per_set_pages is None:
             per_set_pages = w.pool_pages
             w = W.make(3, layer=0, page_base=0)
-            total = per_set_pages * L * W.PAGE * w.row_bytes
-            pool = torch.empty(total, dtype=torch.uint8, device=dev)
+            pool = torch.empty(per_set_pages * L * W.PAGE * w.row_bytes, dtype=torch.uint8, device=dev)
         sets.append((w, upload(w, dev, pool=pool)))
     pool_pages = per_set_pages * L
     torch.cuda.synchronize()
-    print(f"[bench] generated {L} sets of {sets[0][0].name} in {time.time() - t0:.1f}s "
-          f"(pool {pool.numel() / 2**30:.1f} GiB)", file=sys.stderr, flush=True)
+    log(f"generated {L} sets of {sets[0][0].name} in {time.time() - t0:.1f}s "
+        f"(pool {pool.numel() / 2**30:.1f} GiB)")
 
     w0 = sets[0][0]
     B = w0.B
     shape = smla.make_shape(B, w0.kv_format, w0.max_pages, pool_pages)
     plan, ws_bytes = smla.plan_for(shape, args.nsplit or None)
-    plan_arg = plan
     ws = smla.new_workspace(ws_bytes, dev)
     out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 64), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
-    def call(k, fn):
-        d = sets[k % L][1]
-        rc = fn(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, out, lse, shape, plan_arg, ws)
+    def call(d, shp, pl, w_s, o, l_):
+        rc = smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l_, shp, pl, w_s,
+                             stream=stream)
         if rc != 0:
             raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
-
-    def full(*a):
-        return smla.decode_raw(*a)
-
-    def split_only(*a):
-        return smla.split_raw(*a)
 
     def timed(fn, steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -123,52 +155,91 @@ def main() -> int:
         return e0.elapsed_time(e1) * 1000.0 / steps     # us per call
 
     for k in range(args.warmup):
-        call(k, full)
+        call(sets[k % L][1], shape, plan, ws, out, lse)
     torch.cuda.synchronize()
+    runs = [timed(lambda k: call(sets[k % L][1], shape, plan, ws, out, lse), args.steps)
+            for _ in range(args.repeats)]
+    full_us = statistics.median(runs)
+    log(f"B={B} plan={plan.as_dict()} us/call per repeat: {[round(r, 2) for r in runs]}")
 
-    full_us = statistics.median(timed(lambda k: call(k, full), args.steps) for _ in range(args.repeats))
-    split_us = statistics.median(timed(lambda k: call(k, split_only), args.steps) for _ in range(args.repeats))
-    comb_us = None
-    if plan.nsplit > 1:
-        def comb(k):
-            rc = smla.combine_raw(shape, plan_arg, ws, out, lse)
-            if rc != 0:
-                raise RuntimeError(smla.strerror(rc))
-        comb_us = statistics.median(timed(comb, args.steps) for _ in range(args.repeats))
+    alg = [algorithmic(w) for w, _ in sets]
+    call_bytes = float(np.mean([a[0] for a in alg]))
+    call_flops = float(np.mean([a[1] for a in alg]))
+    achieved = call_bytes / (full_us * 1e-6) / 1e9
+    roof_us = max(call_bytes / (HBM_PEAK_GBS * 1e9), call_flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
 
-    byts, flops = zip(*(algorithmic(w, True, plan.nsplit) for w, _ in sets))
-    split_bytes = float(np.mean(byts))
-    split_flops = float(np.mean(flops))
-    all_bytes = float(np.mean([algorithmic(w, False, plan.nsplit)[0] for w, _ in sets]))
-    achieved = split_bytes / (split_us * 1e-6) / 1e9
-    roof_us = max(all_bytes / (HBM_PEAK_GBS * 1e9), split_flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    traffic, traffic_note = None, "no counter file for this kernel source"
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_src") != kernel_source_hash():
+            traffic_note = "kernel changed since the counters were taken"
+        elif t.get("nsplit") != plan.nsplit:
+            traffic_note = "counters were taken at another split count"
+        else:
+            traffic = t.get("hbm_bytes_per_launch")
+            traffic_note = t.get("note", "")
 
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "split_kernel_b80_traffic.json")
-    if os.path.exists(tfile):
-        try:
-            t = json.load(open(tfile))
-            if t.get("plan_nsplit") == plan.nsplit and t.get("kernel_rev") == smla.lib().smla_version():
-                traffic = t.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    # ------------------------------------------------------------------ B sweep
+    sweep = None
+    if not args.no_sweep:
+        t1 = time.time()
+        del sets
+        pool = None
+        torch.cuda.empty_cache()
+        Ls = args.sweep_layers
+        full = []
+        spool, per = None, None
+        for l in range(Ls):
+            w = W.make(5, layer=l, page_base=0 if per is None else l * per)
+            if per is None:
+                per = w.pool_pages
+                w = W.make(5, layer=0, page_base=0)
+                spool = torch.empty(per * Ls * W.PAGE * w.row_bytes, dtype=torch.uint8, device=dev)
+            full.append(w)
+        log(f"generated {Ls} layers of {full[0].name} in {time.time() - t1:.1f}s")
+        per_b = {}
+        for Bs in SWEEP_B:
+            subs = [upload(w.subset(Bs), dev, pool=spool) for w in full]
+            shp = smla.make_shape(Bs, full[0].kv_format, full[0].max_pages, per * Ls)
+            pl, wsb = smla.plan_for(shp)
+            w_s = smla.new_workspace(wsb, dev)
+            o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
+            l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
+            for k in range(10):
+                call(subs[k % Ls], shp, pl, w_s, o, l_)
+            us = statistics.median(timed(lambda k: call(subs[k % Ls], shp, pl, w_s, o, l_), args.sweep_steps)
+                                   for _ in range(3))
+            byts = float(np.mean([algorithmic(w.subset(Bs))[0] for w in full]))
+            per_b[Bs] = {"us_per_layer": round(us, 2), "nsplit": pl.nsplit,
+                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                         "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del subs
+        bs = np.array(SWEEP_B, dtype=float)
+        ys = np.array([per_b[b]["us_per_layer"] for b in SWEEP_B])
+        slope = float(np.polyfit(bs, ys, 1)[0])
+        sweep = {"workload": full[0].name, "ctx_len": int(full[0].ctx_len[0]), "layers_cycled": Ls,
+                 "per_B": {str(k): v for k, v in per_b.items()},
+                 "step_total_us_42_layers": {str(b): round(per_b[b]["us_per_layer"] * LAYERS_PER_STEP, 1)
+                                             for b in SWEEP_B},
+                 "slope_us_per_request_per_layer": round(slope, 3)}
+        log(f"sweep done in {time.time() - t1:.1f}s")
 
+    # ------------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        wc = w0
-        hp = wc.host_pool()
+        hp = w0.host_pool()
         n = 0
         tc = time.time()
         while True:
-            oracle.decode_workload(wc, pool=hp)
+            oracle.decode_workload(w0, pool=hp)
             n += 1
             if time.time() - tc >= args.cpu_seconds:
                 break
-        cpu_us = (time.time() - tc) / n * 1e6
-        cpu = {"value": round(cpu_us, 1), "unit": "us/layer", "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"fp64 C oracle (OpenMP over request x head) on input set 0 of {wc.name} "
-                         f"(B={wc.B}, full batch), {n} calls in {time.time() - tc:.1f}s"}
+        el = time.time() - tc
+        cpu = {"value": round(el / n * 1e6, 1), "unit": "us/layer", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"fp64 C oracle (OpenMP over request x head) on input set 0 of {w0.name} "
+                         f"(B={w0.B}, whole batch), {n} calls in {el:.1f}s"}
 
     res = {
         "metric": METRIC,
@@ -181,21 +252,20 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+        "dtype": "fp8-e4m3 x bf16 mfma, fp32 accum",
+        "data": "synthetic (seeded)",
         "config": {
             "workload": w0.name, "B": B, "heads": 64, "topk": 512, "ctx_len": int(w0.ctx_len[0]),
             "kv_format": "fp8_e4m3_block128+bf16_rope", "row_bytes": w0.row_bytes,
-            "index_mix": "358 of last 8192 tokens + 154 older", "input_sets": L,
-            "plan": plan.as_dict(), "split_us": round(split_us, 3),
-            "combine_us": None if comb_us is None else round(comb_us, 3),
-            "algorithmic_bytes_per_call": int(all_bytes), "algorithmic_flops_per_call": int(split_flops),
+            "index_mix": "358 of the last 8192 tokens + 154 older, without replacement", "input_sets": L,
+            "plan": plan.as_dict(), "repeats_us": [round(r, 3) for r in runs],
+            "algorithmic_bytes_per_call": int(call_bytes), "algorithmic_flops_per_call": int(call_flops),
             "roofline_us_per_call": round(roof_us, 3),
-            "whole_call_frac_of_roofline": round(roof_us / full_us, 4),
-            "whole_call_GBps": round(all_bytes / (full_us * 1e-6) / 1e9, 1),
-            "mfma_frac": round(split_flops / (split_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "mfma_frac_bf16_peak": round(call_flops / (full_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "traffic_note": traffic_note,
+            "sweep": sweep,
         },
-        "roofline": {"kernel": "split_kernel<fp8>", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": KERNEL_NAME, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,

@@ -80,7 +80,7 @@ typedef struct {
 
 /* Launch plan.  Zero fields mean "choose automatically". */
 typedef struct {
-    int32_t nsplit;       /* top-k splits per request (1..16); 1 = no combine kernel      */
+    int32_t nsplit;       /* top-k splits per request (1..16); 1 = no partials, no merge  */
     int32_t tile_tokens;  /* tokens per pipeline tile (only 32 is supported)              */
     int32_t heads_per_wg; /* query heads per workgroup (only 64 is supported)             */
     int32_t wg_per_cu;    /* resident workgroups per compute unit assumed by the selector */
@@ -152,9 +152,11 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
  * sections "Task 1" and "Task 2": one split and one combine kernel per layer).
  *   smla_decode_split takes exactly the arguments of sparse_mla_decode.  With
  *   nsplit = 1 it writes out/lse itself; otherwise it fills the workspace with
- *   per-split partials (fp32 [B, nsplit, 64, 512] normalised outputs, then fp32
- *   [B, nsplit, 64] lse at the next 256-byte boundary) and leaves out/lse and
- *   the arrival counters alone.
+ *   per-split partials (for each (request, split) a 128 KB block holding the
+ *   64 x 512 fp32 output normalised by that split's own softmax denominator,
+ *   in an internal element order that only smla_decode_combine reads; then
+ *   fp32 [B, nsplit, 64] lse at the next 256-byte boundary) and leaves out/lse
+ *   and the arrival counters alone.
  *   smla_decode_combine merges those partials into out/lse; the same shape and
  *   plan must be passed, and it does nothing when the plan has nsplit = 1.
  * Both return as sparse_mla_decode does.

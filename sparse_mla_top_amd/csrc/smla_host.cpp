@@ -63,17 +63,18 @@ size_t workspace_for(int B, int nsplit) {
 // One workgroup is resident per CU (its LDS tiles take most of the 160 KiB),
 // so B * nsplit workgroups run in ceil(B*nsplit / cus) dispatch rounds, each
 // as long as the longest split (chunk tiles of 32 tokens).  Splitting also
-// writes and re-reads a normalised fp32 partial per (request, split, head)
-// and adds the combine launch.  The constants are calibrated on MI355X.
+// writes and re-reads a normalised fp32 partial per (request, split, head),
+// merged by the last split of each request to finish.  The constants are
+// fitted to MI355X timings of the fused kernel on cold caches.
 double est_time_us(int B, int nsplit, int chunk_tiles, int cus) {
-  const double t_fixed = 2.0;     // translation + first-gather latency per workgroup
-  const double t_tile = 0.45;     // one 32-token tile for 64 heads on one CU
-  const double t_comb = 1.5;      // combine launch + latency
-  const double part_bw = 6.0e6;   // bytes per us for partial traffic
+  const double t_start = 9.3;     // launch, translation and first-gather latency per workgroup
+  const double t_tile = 1.27;     // one 32-token tile for 64 heads on one CU
+  const double t_merge0 = 6.3;    // arrival, coherent partial write/read latency of the merge
+  const double t_merge_split = 1.6;  // per partial read by the merging workgroup
   const int grid = B * nsplit;
   const int rounds = (grid + cus - 1) / cus;
-  double t = rounds * (t_fixed + chunk_tiles * t_tile);
-  if (nsplit > 1) t += t_comb + 2.0 * grid * (double)kHeads * (kDv + 1) * 4.0 / part_bw;
+  double t = rounds * (t_start + chunk_tiles * t_tile);
+  if (nsplit > 1) t += t_merge0 + t_merge_split * nsplit;
   return t;
 }
 
@@ -87,7 +88,7 @@ int smla_row_bytes(int kv_format) {
   return -1;
 }
 
-int smla_version(void) { return 100; }
+int smla_version(void) { return 101; }
 
 const char* smla_strerror(int code) {
   switch (code) {

@@ -183,6 +183,38 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Partial results travel between workgroups of one launch that may sit on
+// different XCDs, whose L2 caches are not kept coherent with each other.
+// Stores and loads carrying device scope (sc1) are made coherent by the
+// hardware on their own, so no device-scope fence is needed: such a fence
+// writes back or invalidates a whole L2.  Buffer accesses are used so each
+// wave moves whole 1 KB runs (write-through at dword or 32-byte granularity
+// would flood the memory system with partial-line writes).
+constexpr int kSc1 = 16;                     // cache-policy bit: device scope
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every global store this wave issued has completed.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Layout of one (request, split) partial output, 64 x 512 fp32 = 128 KB, in
+// 128 runs of 1 KB.  Run c = ((vb * 4 + db) * 4 + jj) * 2 + hb holds, at
+// float4 slot lane = l32 + 32 kg, dims 128vb + 32db + 8jj + 4kg + 0..3 of head
+// 32hb + l32: exactly what lane `lane` of the PV wave owning latent slice vb
+// keeps in registers 4jj..4jj+3 of accumulator [db][hb].
+__device__ __forceinline__ uint32_t part_run_offset(int vb, int db, int jj, int hb, int lane) {
+  return ((((vb * 4 + db) * 4 + jj) * 2 + hb) * 256 + lane * 4) * 4;     // bytes
+}
+constexpr uint32_t kPartBytes = kHeads * kDv * 4;
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
@@ -202,42 +234,70 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 // workgroup: out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
 // M = max_s lse_s, lse = M + ln sum_s w_s; all splits empty -> out 0, lse -inf.
 // Thread t owns head t/8 and dims 64(t%8) .. +63.
+// Merge the nsplit partials of request b (512 threads):
+//   out = sum_s w_s O_s,  w_s = exp(lse_s - M) / sum_r exp(lse_r - M),
+//   lse = M + ln sum_r exp(lse_r - M),  M = max_s lse_s;
+// every split empty -> out 0, lse -inf.  wt is 16 x 64 floats of LDS.
 __device__ __forceinline__ void merge_request(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                              int nsplit, int b, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int h = threadIdx.x >> 3, d0 = 64 * (threadIdx.x & 7);
-  const float* ls = part_lse + (int64_t)b * nsplit * kHeads + h;
-  float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ls[sp * kHeads]);
-  float acc[64];
-#pragma unroll
-  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
-  float wsum = 0.f;
-  if (M != -INFINITY) {
+                                              int nsplit, int b, uint16_t* __restrict__ out, float* __restrict__ lse,
+                                              float* wt) {
+  const int t = threadIdx.x;
+  if (t < kHeads) {
+    const float* ls = part_lse + (int64_t)b * nsplit * kHeads + t;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, load_agent(ls + sp * kHeads));
+    float wsum = 0.f;
     for (int sp = 0; sp < nsplit; ++sp) {
-      const float l = ls[sp * kHeads];
-      if (l == -INFINITY) continue;
-      const float wgt = __expf(l - M);
-      wsum += wgt;
-      const float4* src = reinterpret_cast<const float4*>(part_o + (((int64_t)b * nsplit + sp) * kHeads + h) * kDv + d0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 v = src[i];
-        acc[4 * i] += wgt * v.x; acc[4 * i + 1] += wgt * v.y; acc[4 * i + 2] += wgt * v.z; acc[4 * i + 3] += wgt * v.w;
-      }
+      const float e = M == -INFINITY ? 0.f : __expf(load_agent(ls + sp * kHeads) - M);
+      wt[sp * kHeads + t] = e;
+      wsum += e;
     }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) wt[sp * kHeads + t] *= inv;
+    lse[(int64_t)b * kHeads + t] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
   }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  uint16_t* orow = out + ((int64_t)b * kHeads + h) * kDv + d0;
+  lds_barrier();
+  // wave w merges runs of latent slice vb = w/2, 32-dim blocks db = 2(w%2) + 0..1
+  const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
+  const int vb = wave >> 1, db0 = 2 * (wave & 1);
+  f32x4 acc[2][4][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint4 w4;
-    w4.x = (uint32_t)f32_to_bf16_rne(acc[8 * i] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 1] * inv) << 16);
-    w4.y = (uint32_t)f32_to_bf16_rne(acc[8 * i + 2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 3] * inv) << 16);
-    w4.z = (uint32_t)f32_to_bf16_rne(acc[8 * i + 4] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 5] * inv) << 16);
-    w4.w = (uint32_t)f32_to_bf16_rne(acc[8 * i + 6] * inv) | ((uint32_t)f32_to_bf16_rne(acc[8 * i + 7] * inv) << 16);
-    *reinterpret_cast<uint4*>(orow + 8 * i) = w4;
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) acc[i][j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const __amdgpu_buffer_rsrc_t r = buffer_of(part_o + ((int64_t)b * nsplit + sp) * (kHeads * kDv), kPartBytes);
+    const float w0 = wt[sp * kHeads + l32], w1 = wt[sp * kHeads + 32 + l32];
+    f32x4 v[2][4][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          v[i][j][hb] = __builtin_amdgcn_raw_buffer_load_b128(r, part_run_offset(vb, db0 + i, j, hb, lane), 0, kSc1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j][0] += w0 * v[i][j][0];
+        acc[i][j][1] += w1 * v[i][j][1];
+      }
   }
-  if ((threadIdx.x & 7) == 0) lse[(int64_t)b * kHeads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const f32x4 x = acc[i][j][hb];
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+        uint16_t* orow = out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 32 * (db0 + i) + 8 * j + 4 * kg;
+        *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
+      }
 }
 
 // ----------------------------------------------------------------------------
@@ -547,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       fin_s[head] = L;
       const float lse_v = L > 0.f ? (m_run + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
       if (a.nsplit == 1) a.lse[(int64_t)b * kHeads + head] = lse_v;
-      else a.part_lse[((int64_t)b * a.nsplit + s) * kHeads + head] = lse_v;
+      else store_agent(a.part_lse + ((int64_t)b * a.nsplit + s) * kHeads + head, lse_v);
     }
     lds_barrier();
   } else {
@@ -666,64 +726,41 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           }
       }
     } else {
+      const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)b * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float* prow = a.part_o + (((int64_t)b * a.nsplit + s) * kHeads + 32 * hb + l32) * kDv + 128 * vb + 4 * kg;
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            *reinterpret_cast<float4*>(prow + 32 * db + 8 * jj) =
-                make_float4(o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb],
-                            o[db][hb][4 * jj + 2] * inv[hb], o[db][hb][4 * jj + 3] * inv[hb]);
+            const f32x4 v = {o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb],
+                             o[db][hb][4 * jj + 2] * inv[hb], o[db][hb][4 * jj + 3] * inv[hb]};
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, kSc1);
           }
-      }
     }
   }
 
   // ---- fused combine: the last split of a request to finish merges them
   if (a.nsplit > 1 && a.counters != nullptr) {
-    __threadfence();                     // this workgroup's partials, device-visible
+    wait_stores();                       // this wave's partials are device-visible
+    lds_barrier();                       // ... and so are every other wave's
+    if (threadIdx.x == 0)
+      last_s = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(a.nsplit - 1);
     lds_barrier();
-    if (threadIdx.x == 0) last_s = atomicAdd(&a.counters[b], 1u) == (uint32_t)(a.nsplit - 1);
-    lds_barrier();
-    if (last_s) {
-      __threadfence();                   // acquire the other splits' partials
-      merge_request(a.part_o, a.part_lse, a.nsplit, b, a.out, a.lse);
+    if (last_s) {                        // every split has arrived; their partials are read coherently
+      merge_request(a.part_o, a.part_lse, a.nsplit, b, a.out, a.lse, &p_s[0][0][0]);
       if (threadIdx.x == 0) a.counters[b] = 0u;   // ready for the next call
     }
   }
 }
 
 // ----------------------------------------------------------------------------
-// Combine: out[b,h,:] = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
-// lse = M + ln sum_s w_s; all splits empty -> out 0, lse -inf.
-// One 128-thread block per (request, head); thread t owns dims 4t..4t+3.
-__global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  const int bh = blockIdx.x;                 // b * 64 + h
-  const int b = bh >> 6, h = bh & 63;
-  const float* lse_s = a.part_lse + (int64_t)b * a.nsplit * kHeads + h;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, lse_s[s * kHeads]);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ls = lse_s[s * kHeads];
-      if (ls == -INFINITY) continue;
-      const float wgt = __expf(ls - M);
-      wsum += wgt;
-      const float4 v = *reinterpret_cast<const float4*>(
-          a.part_o + (((int64_t)b * a.nsplit + s) * kHeads + h) * kDv + 4 * threadIdx.x);
-      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
-    }
-  }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  uint16_t* orow = a.out + ((int64_t)b * kHeads + h) * kDv + 4 * threadIdx.x;
-  const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
-  *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
-  if (threadIdx.x == 0) a.lse[(int64_t)b * kHeads + h] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+// Combine as a launch of its own: one 512-thread workgroup per request runs
+// the same merge as the fused path, so both give identical bits.
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  __shared__ float wt[16 * kHeads];
+  merge_request(a.part_o, a.part_lse, a.nsplit, blockIdx.x, a.out, a.lse, wt);
 }
 
 // ----------------------------------------------------------------------------
@@ -760,7 +797,7 @@ hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t st
 }
 
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(B * kHeads), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(B), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
