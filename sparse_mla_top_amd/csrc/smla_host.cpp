@@ -50,13 +50,13 @@ int check_shape(const smla_shape* s) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout (nsplit > 1): fp32 partial outputs [B, nsplit, 64, 512],
-// fp32 partial lse [B, nsplit, 64], uint32 arrival counters [B]; each region
-// starts at a 256-byte boundary.
+// fp32 partial lse [B, nsplit, 64], uint32 counters [B][2] (arrival tickets,
+// finished partial writes); each region starts at a 256-byte boundary.
 size_t ws_part_o_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * kDv * sizeof(float)); }
 size_t ws_part_lse_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * sizeof(float)); }
 size_t workspace_for(int B, int nsplit) {
   if (nsplit <= 1 || B == 0) return 0;
-  return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * sizeof(uint32_t));
+  return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * 2 * sizeof(uint32_t));
 }
 
 // Estimated time (us) of one call with `nsplit` splits on `cus` compute units.

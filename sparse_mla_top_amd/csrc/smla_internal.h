@@ -38,7 +38,7 @@ struct SplitArgs {
   float* part_lse;             // [B][nsplit][64] natural-log lse of each split
   uint16_t* out;               // bf16 [B][64][512] (written directly when nsplit == 1)
   float* lse;                  // [B][64]
-  uint32_t* counters;          // [B] arrival counters; non-null: the last split merges
+  uint32_t* counters;          // [B][2] tickets / finished writes; non-null: the last split merges
 };
 
 struct CombineArgs {

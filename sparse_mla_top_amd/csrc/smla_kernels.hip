@@ -214,6 +214,9 @@ __device__ __forceinline__ uint32_t part_run_offset(int vb, int db, int jj, int 
   return ((((vb * 4 + db) * 4 + jj) * 2 + hb) * 256 + lane * 4) * 4;     // bytes
 }
 constexpr uint32_t kPartBytes = kHeads * kDv * 4;
+// Polls of the finished-writes counter before a merging workgroup gives up
+// (never reached when every split runs: they are all past their compute).
+constexpr int kSpinLimit = 1 << 22;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
@@ -234,30 +237,35 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 // workgroup: out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - M),
 // M = max_s lse_s, lse = M + ln sum_s w_s; all splits empty -> out 0, lse -inf.
 // Thread t owns head t/8 and dims 64(t%8) .. +63.
-// Merge the nsplit partials of request b (512 threads):
-//   out = sum_s w_s O_s,  w_s = exp(lse_s - M) / sum_r exp(lse_r - M),
-//   lse = M + ln sum_r exp(lse_r - M),  M = max_s lse_s;
-// every split empty -> out 0, lse -inf.  wt is 16 x 64 floats of LDS.
-__device__ __forceinline__ void merge_request(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                              int nsplit, int b, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                              float* wt) {
-  const int t = threadIdx.x;
-  if (t < kHeads) {
-    const float* ls = part_lse + (int64_t)b * nsplit * kHeads + t;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, load_agent(ls + sp * kHeads));
-    float wsum = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float e = M == -INFINITY ? 0.f : __expf(load_agent(ls + sp * kHeads) - M);
-      wt[sp * kHeads + t] = e;
-      wsum += e;
-    }
-    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) wt[sp * kHeads + t] *= inv;
-    lse[(int64_t)b * kHeads + t] = wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+// Softmax weights of the nsplit partials of one head, written to
+// wt[sp * kHeads] (normalised: they sum to 1), and the merged lse:
+//   w_s = exp(lse_s - M) / sum_r exp(lse_r - M),  M = max_s lse_s,
+//   lse = M + ln sum_r exp(lse_r - M);  every split empty -> w = 0, lse = -inf.
+// Both merge paths call this, so they round identically.
+template <class LseOf>
+__device__ __forceinline__ float split_weights(int nsplit, LseOf lse_of, float* wt) {
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, lse_of(sp));
+  float wsum = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float e = M == -INFINITY ? 0.f : __expf(lse_of(sp) - M);
+    wt[sp * kHeads] = e;
+    wsum += e;
   }
-  lds_barrier();
-  // wave w merges runs of latent slice vb = w/2, 32-dim blocks db = 2(w%2) + 0..1
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) wt[sp * kHeads] *= inv;
+  return wsum > 0.f ? M + __logf(wsum) : -INFINITY;
+}
+
+// Merge the nsplit partials of request b (512 threads, weights already in
+// wt[sp * kHeads + head]): out = sum_s w_s O_s, accumulated in split order.
+// run_of(sp, byte_offset) returns the float4 of partial sp at that offset of
+// its 128 KB block.  Wave w takes latent slice vb = w/2 and 32-dim blocks
+// 2(w%2) + 0..1, i.e. 16 runs; the runs of two splits are loaded together.
+template <class RunOf>
+__device__ __forceinline__ void merge_runs(int nsplit, int b, uint16_t* __restrict__ out, const float* wt,
+                                           RunOf run_of) {
+  const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
   const int vb = wave >> 1, db0 = 2 * (wave & 1);
   f32x4 acc[2][4][2];
@@ -267,24 +275,31 @@ __device__ __forceinline__ void merge_request(const float* __restrict__ part_o, 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) acc[i][j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const __amdgpu_buffer_rsrc_t r = buffer_of(part_o + ((int64_t)b * nsplit + sp) * (kHeads * kDv), kPartBytes);
-    const float w0 = wt[sp * kHeads + l32], w1 = wt[sp * kHeads + 32 + l32];
-    f32x4 v[2][4][2];
+  for (int sp = 0; sp < nsplit; sp += 2) {
+    const bool two = sp + 1 < nsplit;
+    f32x4 v[2][2][4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          v[i][j][hb] = __builtin_amdgcn_raw_buffer_load_b128(r, part_run_offset(vb, db0 + i, j, hb, lane), 0, kSc1);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+          for (int hb = 0; hb < 2; ++hb)
+            v[u][i][j][hb] = (u == 0 || two) ? run_of(sp + u, part_run_offset(vb, db0 + i, j, hb, lane))
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j][0] += w0 * v[i][j][0];
-        acc[i][j][1] += w1 * v[i][j][1];
-      }
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      const float w0 = wt[(sp + u) * kHeads + l32], w1 = wt[(sp + u) * kHeads + 32 + l32];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j][0] += w0 * v[u][i][j][0];
+          acc[i][j][1] += w1 * v[u][i][j][1];
+        }
+    }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -300,8 +315,133 @@ __device__ __forceinline__ void merge_request(const float* __restrict__ part_o, 
       }
 }
 
+// Weights of request b's splits into wt (16 x 64 floats of LDS) and the merged
+// lse into lse[b, :] (512 threads).  lse_of(sp, h) gives split sp's lse of
+// head h; all of them are fetched in one parallel pass first.
+template <class LseOf>
+__device__ __forceinline__ void merge_weights(int nsplit, int b, float* __restrict__ lse, float* wt, LseOf lse_of) {
+  for (int i = threadIdx.x; i < nsplit * kHeads; i += kThreads) wt[i] = lse_of(i >> 6, i & (kHeads - 1));
+  lds_barrier();
+  const int t = threadIdx.x;
+  if (t < kHeads)    // in place: column t is read before it is overwritten
+    lse[(int64_t)b * kHeads + t] = split_weights(nsplit, [&](int sp) { return wt[sp * kHeads + t]; }, wt + t);
+  lds_barrier();
+}
+
+__device__ __forceinline__ f32x4 load_run(const float* part_o, int64_t block, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = buffer_of(part_o + block * (kHeads * kDv), kPartBytes);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
+}
+
+// Merge the nsplit partials of request b from the workspace (512 threads).
+// wt is 16 x 64 floats of LDS.
+__device__ __forceinline__ void merge_request(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                              int nsplit, int b, uint16_t* __restrict__ out, float* __restrict__ lse,
+                                              float* wt) {
+  const float* ls = part_lse + (int64_t)b * nsplit * kHeads;
+  merge_weights(nsplit, b, lse, wt, [&](int sp, int h) { return load_agent(ls + sp * kHeads + h); });
+  merge_runs(nsplit, b, out, wt,
+             [&](int sp, uint32_t off) { return load_run(part_o, (int64_t)b * nsplit + sp, off); });
+}
+
+// The fused merge of request b by its last split `own` (512 threads).  Its
+// own partial is in LDS (`own_part`, workspace-block layout) with its lse in
+// own_lse[h]; the other nsplit - 1 partials and lses are in the workspace.
+// Same weights and the same split-ordered accumulation as merge_request, but
+// the lse loads and the first partial loads go out together, and each round
+// loads two partials other than the own one: one memory round trip when
+// nsplit <= 3.
+__device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                            int nsplit, int b, int own, const uint8_t* own_part, const float* own_lse,
+                                            uint16_t* __restrict__ out, float* __restrict__ lse, float* wt) {
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
+  const int vb = wave >> 1, db0 = 2 * (wave & 1);
+  const int nother = nsplit - 1;
+  auto other = [&](int k) { return k < own ? k : k + 1; };    // k-th split other than own, ascending
+  const float* ls = part_lse + (int64_t)b * nsplit * kHeads;
+
+  // lse of every split (at most two per thread), issued first
+  float lv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = t + u * kThreads, sp = i >> 6, h = i & (kHeads - 1);
+    lv[u] = i < nsplit * kHeads ? (sp == own ? own_lse[h] : load_agent(ls + sp * kHeads + h)) : 0.f;
+  }
+  f32x4 v[2][2][4][2];
+  auto issue = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            v[u][i][j][hb] = k0 + u < nother
+                                 ? load_run(part_o, (int64_t)b * nsplit + other(k0 + u),
+                                            part_run_offset(vb, db0 + i, j, hb, lane))
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  issue(0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (t + u * kThreads < nsplit * kHeads) wt[t + u * kThreads] = lv[u];
+  lds_barrier();
+  if (t < kHeads)
+    lse[(int64_t)b * kHeads + t] = split_weights(nsplit, [&](int sp) { return wt[sp * kHeads + t]; }, wt + t);
+  lds_barrier();
+
+  f32x4 acc[2][4][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) acc[i][j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto add = [&](int sp, auto&& val) {
+    const float w0 = wt[sp * kHeads + l32], w1 = wt[sp * kHeads + 32 + l32];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j][0] += w0 * val(i, j, 0);
+        acc[i][j][1] += w1 * val(i, j, 1);
+      }
+  };
+  auto own_val = [&](int i, int j, int hb) {
+    return *reinterpret_cast<const f32x4*>(own_part + part_run_offset(vb, db0 + i, j, hb, lane));
+  };
+  bool own_done = false;
+  for (int k0 = 0; k0 < nother; k0 += 2) {
+    if (k0 > 0) issue(k0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (k0 + u >= nother) break;
+      const int sp = other(k0 + u);
+      if (!own_done && own < sp) {
+        add(own, own_val);
+        own_done = true;
+      }
+      add(sp, [&](int i, int j, int hb) { return v[u][i][j][hb]; });
+    }
+  }
+  if (!own_done) add(own, own_val);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const f32x4 x = acc[i][j][hb];
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+        uint16_t* orow = out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 32 * (db0 + i) + 8 * j + 4 * kg;
+        *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
+      }
+}
+
 // ----------------------------------------------------------------------------
-// Split kernel.  512 threads// ----------------------------------------------------------------------------
 // Split kernel.  512 threads = 8 waves, one workgroup per (request, split),
 // with two roles that run side by side on each SIMD (waves w and w+4 share
 // SIMD w):
@@ -333,15 +473,23 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   constexpr int kRow = RowFmt<FMT>::kRow;
   constexpr int kNbuf = RowFmt<FMT>::kNbuf;
   constexpr int kTileBytes = kTile * kRow;
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kNbuf * kTileBytes];
+  // One LDS block: the tile ring, then P^T.  A merging workgroup reuses its
+  // first 128 KB for its own partial output.
+  constexpr int kRingBytes = kNbuf * kTileBytes;
+  constexpr int kPBytes = 2 * kHeads * kPRow * 4;
+  constexpr int kSmem = kRingBytes + kPBytes > (int)kPartBytes ? kRingBytes + kPBytes : (int)kPartBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+  uint8_t* const tiles = smem;
   __shared__ uint64_t rowaddr_s[kTopk];            // row address | 1 when masked
   __shared__ uint32_t mask_s[kTiles];              // bit t: token t of the tile is valid
   // P^T (fp32, unscaled) in [head][token] rows padded to 36 floats so the
   // 16-byte accesses of 8 consecutive lanes hit distinct banks
-  __shared__ __attribute__((aligned(16))) float p_s[2][kHeads][kPRow];
+  float (*const p_s)[kHeads][kPRow] = reinterpret_cast<float (*)[kHeads][kPRow]>(smem + kRingBytes);
   __shared__ float alpha_s[2][kHeads];
   __shared__ float fin_s[kHeads];
   __shared__ int last_s;
+  __shared__ float lsev_s[kHeads];                 // this split's lse per head
+  __shared__ int fail_s;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -357,6 +505,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int ntiles = min(a.chunk_tiles, kTiles - tile0);
   const int ntok = ntiles * kTile;
   const int ctx = a.ctx_len[b];
+  const bool fused = a.nsplit > 1 && a.counters != nullptr;   // merge in this launch
 
   // ---- 1. QK waves: raw Q of their 16 heads (lane column = head)
   const int head = (wave & 3) * 16 + c16;
@@ -409,10 +558,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // ---- 3. the PV waves issue every tile load (the QK waves never wait on
   // the texture path); first the prefetch of the first kNbuf tiles
   const int vwave = wave & 3;
-  // kAhead tiles are in flight beyond the one being scored: tile k + kAhead is
-  // issued at iteration k into the buffer of tile k - 2 (scored at k - 2,
-  // accumulated at k - 1, so free after the barrier of iteration k).
+  // In iteration k the QK waves start tile k+1 and finish tile k, and the PV
+  // waves accumulate tile k-1; tile k + kAhead is issued at the top of
+  // iteration k into the buffer of tile k - 2 (finished at k - 2, accumulated
+  // at k - 1, so free after the barrier of iteration k).
   constexpr int kAhead = kNbuf - 2;
+  // The QK look-ahead needs tile k+1 issued before iteration k, i.e. a ring of
+  // at least 4 buffers (fp8 rows: 6; bf16 rows fit only 3 and run unpipelined,
+  // tile k scored and finished in iteration k).
+  constexpr bool kPipe = kNbuf >= 4;
   const int npre = min(kAhead, ntiles);
   if (!qk_role)
     for (int tt = 0; tt < npre; ++tt)
@@ -422,10 +576,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // Top of iteration k: the PV waves wait for their share of tile k, then a
   // barrier publishes it; then they issue tile k + kAhead.
   auto iteration_head = [&](int k) {
-    if (!qk_role && k < ntiles) {
-      const int after = min(ntiles, k + kAhead) - k - 1;   // tiles issued after tile k
+    const int need = kPipe ? k + 1 : k;   // the tile the QK waves start in iteration k
+    if (!qk_role && need < ntiles) {
+      const int after = min(ntiles, k + kAhead) - need - 1;   // tiles issued after it
       if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(after);
       else wait_tiles<DmaCount<FMT>::of(3)>(after);
+    } else if (!qk_role && k < ntiles) {
+      if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(0);
+      else wait_tiles<DmaCount<FMT>::of(3)>(0);
     }
     lds_barrier();
     if (!qk_role && k + kAhead < ntiles)
@@ -487,29 +645,35 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     float m_run = -INFINITY;        // running max (log2 domain) of this lane's head
     float l_run = 0.f;              // this lane's share of the running sum
 
-    // Iteration k = -1 is a warm-up pass through the same loop code on
-    // whatever buffer 0 holds, with every slot masked and its state thrown
-    // away: it pulls the loop's instructions into the instruction cache while
-    // the first tile is still in flight.  Its P/alpha writes land in buffer 0,
-    // which the real iteration 0 overwrites before any PV wave reads it.
-    const int kfirst = __builtin_amdgcn_readfirstlane(a.nsplit > 0 ? -1 : 0);
-#pragma clang loop unroll(disable)
-    for (int k = kfirst; k <= ntiles; ++k) {
-      const bool dry = k < 0;
-      if (!dry) iteration_head(k);
-      if (k == ntiles) break;
-      const int kt = dry ? 0 : k;
+    // Scores are software-pipelined: in iteration k the MFMAs of tile k+1
+    // are issued before the softmax of tile k (whose MFMA results came from
+    // iteration k-1), so the matrix pipe runs under the softmax's VALU and
+    // cross-lane work.  Raw holds one tile's accumulators before the fp8
+    // block scales, which are applied when the tile is finished.
+    struct Raw {
+      f32x4 acc[2][FMT == kFmtFp8 ? 4 : 1];   // [16-token half][scale block] (fp8 rows only)
+      f32x4 sm[2];       // rope part (fp8 rows) or the whole score (bf16 rows)
+    };
+    auto issue_scores = [&](int kt, Raw& r) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
-      const uint32_t vmask = dry ? 0u : mask_s[kt];
-
-      // all operand reads of both 16-token halves first
-      i32x8 ka[2][4];
-      bf16x8 kr[2][18];
-      float4 sv[2][4];
+      if constexpr (FMT == kFmtBf16) {
+        // one 16-token half at a time (18 operand registers of 4 each)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint8_t* krow = tb + (16 * m + c16) * kRow;
-        if constexpr (FMT == kFmtFp8) {
+        for (int m = 0; m < 2; ++m) {
+          const uint8_t* krow = tb + (16 * m + c16) * kRow;
+          f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 18; ++c)
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(krow + 2 * (32 * c + 8 * g)),
+                                                        qb[c], sm, 0, 0, 0);
+          r.sm[m] = sm;
+        }
+      } else {
+        i32x8 ka[2][4];
+        bf16x8 kr[2][2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint8_t* krow = tb + (16 * m + c16) * kRow;
 #pragma unroll
           for (int blk = 0; blk < 4; ++blk) {
             const i32x4 k0 = *reinterpret_cast<const i32x4*>(krow + 128 * blk + 32 * g);
@@ -518,43 +682,41 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           }
 #pragma unroll
           for (int c = 0; c < 2; ++c)
-            kr[m][16 + c] = *reinterpret_cast<const bf16x8*>(krow + kDl + 16 + 2 * (32 * c + 8 * g));
+            kr[m][c] = *reinterpret_cast<const bf16x8*>(krow + kDl + 16 + 2 * (32 * c + 8 * g));
+        }
+        // independent MFMA chains per half: hi of every block, rope, then lo
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sv[m][i] = *reinterpret_cast<const float4*>(tb + (16 * m + 4 * g + i) * kRow + kDl);
-        } else {
+        for (int m = 0; m < 2; ++m) {
+          f32x4 sm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < 18; ++c)
-            kr[m][c] = *reinterpret_cast<const bf16x8*>(krow + 2 * (32 * c + 8 * g));
+          for (int blk = 0; blk < 4; ++blk)
+            r.acc[m][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qhi[blk],
+                                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m][c], qb[16 + c], sm, 0, 0, 0);
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk)
+            r.acc[m][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qlo[blk], r.acc[m][blk], 0, 0,
+                                                                            0, 0, 0, 0);
+          r.sm[m] = sm;
         }
       }
-
-      // scores S^T for the two 16-token halves: independent MFMA chains
-      // (hi of every block, rope, then lo), block scales last
+    };
+    // softmax of tile kt from its raw scores; P^T and alpha to LDS
+    auto finish_tile = [&](int kt, bool dry, const Raw& r) {
+      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+      const uint32_t vmask = dry ? 0u : mask_s[kt];
       f32x4 sacc[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sm = r.sm[m];
         if constexpr (FMT == kFmtFp8) {
-          f32x4 acc[4];
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-            acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qhi[blk], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m][16 + c], qb[16 + c], sm, 0, 0, 0);
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-            acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qlo[blk], acc[blk], 0, 0, 0, 0, 0, 0);
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm[i] += acc[blk][i] * (&sv[m][i].x)[blk];
-        } else {
-#pragma unroll
-          for (int c = 0; c < 18; ++c)
-            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m][c], qb[c], sm, 0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            const float4 sv = *reinterpret_cast<const float4*>(tb + (16 * m + 4 * g + i) * kRow + kDl);
+            sm[i] += r.acc[m][0][i] * sv.x + r.acc[m][1][i] * sv.y + r.acc[m][2][i] * sv.z + r.acc[m][3][i] * sv.w;
+          }
         }
         sacc[m] = sm;
       }
@@ -599,17 +761,63 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         *reinterpret_cast<float4*>(&p_s[pb][head][16 * m + 4 * g]) =
             make_float4(p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]);
       if (g == 0) alpha_s[pb][head] = alpha;
+    };
+    // One iteration: k = -1 is a warm-up pass through the same code on
+    // whatever buffer 0 holds, every slot masked and its state thrown away,
+    // which pulls the loop's instructions into the instruction cache while the
+    // first tiles are in flight (its P/alpha writes land in buffer 0, which
+    // iteration 0 overwrites before any PV wave reads it).  Iteration k >= 0
+    // finishes tile k (scores in `cur`) and starts tile k+1 (into `nxt`).
+    auto body = [&](int k, Raw& cur, Raw& nxt) {
+      const bool dry = k < 0;
+      if constexpr (kPipe) {   // (the bf16 ring runs the unpipelined loop below)
+        if (k <= 0) {
+          if (!dry) iteration_head(0);
+          issue_scores(0, cur);
+        }
+        if (k + 1 < ntiles) issue_scores(k + 1, nxt);
+        finish_tile(dry ? 0 : k, dry, cur);
+        if (!dry) iteration_head(k + 1);
+      }
+    };
+    Raw ra, rb;
+    const int kfirst = __builtin_amdgcn_readfirstlane(a.nsplit > 0 ? -1 : 0);
+    if constexpr (kPipe) {
+      // unrolled by two so the raw scores alternate between ra and rb
+#pragma clang loop unroll(disable)
+      for (int k = kfirst; k < ntiles; k += 2) {
+        body(k, ra, rb);
+        if (k + 1 < ntiles) body(k + 1, rb, ra);
+      }
+    } else {
+#pragma clang loop unroll(disable)
+      for (int k = kfirst; k <= ntiles; ++k) {
+        const bool dry = k < 0;
+        if (!dry) iteration_head(k);
+        if (k == ntiles) break;
+        Raw r;
+        issue_scores(dry ? 0 : k, r);
+        finish_tile(dry ? 0 : k, dry, r);
+      }
     }
 
+    // This split's scores are done (only the PV waves' last tile is left,
+    // which waits on nothing): take the request's arrival ticket now, so its
+    // latency overlaps that tile.  The holder of the last ticket merges.
+    if (fused && threadIdx.x == 0)
+      last_s = __hip_atomic_fetch_add(&a.counters[2 * b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(a.nsplit - 1);
     // normaliser of each head for the PV waves; lse from here
     const float L = wave_sum16(l_run);
+    const float lse_v = L > 0.f ? (m_run + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
     if (g == 0) {
       fin_s[head] = L;
-      const float lse_v = L > 0.f ? (m_run + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+      lsev_s[head] = lse_v;
       if (a.nsplit == 1) a.lse[(int64_t)b * kHeads + head] = lse_v;
-      else store_agent(a.part_lse + ((int64_t)b * a.nsplit + s) * kHeads + head, lse_v);
     }
     lds_barrier();
+    if (a.nsplit > 1 && !(fused && last_s) && g == 0)
+      store_agent(a.part_lse + ((int64_t)b * a.nsplit + s) * kHeads + head, lse_v);
   } else {
     // ---------------------------------------------------------------- PV role
     // 32x32x16 bf16 MFMA: O^T[32 d][32 heads] += V^T[32 d][16 tok] . P^T[16 tok][32 heads].
@@ -725,7 +933,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
             *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
           }
       }
-    } else {
+    } else if (!fused || !last_s) {
       const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)b * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -737,22 +945,47 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
                              o[db][hb][4 * jj + 2] * inv[hb], o[db][hb][4 * jj + 3] * inv[hb]};
             __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, kSc1);
           }
+    } else {
+      // last split of the request: its own partial goes to LDS, in the
+      // layout of a workspace block
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, db, jj, hb, lane)) =
+                f32x4{o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb], o[db][hb][4 * jj + 2] * inv[hb],
+                      o[db][hb][4 * jj + 3] * inv[hb]};
     }
   }
 
-  // ---- fused combine: the last split of a request to finish merges them
-  if (a.nsplit > 1 && a.counters != nullptr) {
-    wait_stores();                       // this wave's partials are device-visible
-    lds_barrier();                       // ... and so are every other wave's
+  // ---- fused merge
+  if (!fused) return;
+  if (!last_s) {
+    wait_stores();                       // this wave's partial stores have completed ...
+    lds_barrier();                       // ... and so have every other wave's
     if (threadIdx.x == 0)
-      last_s = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(a.nsplit - 1);
-    lds_barrier();
-    if (last_s) {                        // every split has arrived; their partials are read coherently
-      merge_request(a.part_o, a.part_lse, a.nsplit, b, a.out, a.lse, &p_s[0][0][0]);
-      if (threadIdx.x == 0) a.counters[b] = 0u;   // ready for the next call
-    }
+      __hip_atomic_fetch_add(&a.counters[2 * b + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
+  // Last ticket: wait until the splits with earlier tickets (all resident and
+  // past their compute) have finished writing, then merge with all 8 waves,
+  // this split's own partial and lse read from LDS.
+  if (threadIdx.x == 0) {
+    bool ok = false;
+    for (int it = 0; it < kSpinLimit && !ok; ++it) {
+      ok = __hip_atomic_load(&a.counters[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+           (uint32_t)(a.nsplit - 1);
+      if (!ok) __builtin_amdgcn_s_sleep(2);
+    }
+    fail_s = ok ? 0 : 1;
+    a.counters[2 * b] = 0u;              // both counters back to zero for the next call
+    a.counters[2 * b + 1] = 0u;
+  }
+  lds_barrier();
+  merge_fused(a.part_o, a.part_lse, a.nsplit, b, s, smem, lsev_s, a.out, a.lse, reinterpret_cast<float*>(rowaddr_s));
+  if (fail_s && threadIdx.x < kHeads) a.lse[(int64_t)b * kHeads + threadIdx.x] = __builtin_nanf("");
 }
 
 // ----------------------------------------------------------------------------

@@ -87,8 +87,8 @@ def test_forced_nsplit_normalised_to_whole_tiles(forced, expect):
     chunk = math.ceil(16 / p.nsplit)
     assert (p.nsplit - 1) * chunk < 16 <= p.nsplit * chunk
     a256 = lambda x: (x + 255) // 256 * 256
-    # partial outputs, partial lse, one arrival counter per request
-    assert ws == (0 if expect == 1 else a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4) + a256(8 * 4))
+    # partial outputs, partial lse, two counters per request (tickets, finished writes)
+    assert ws == (0 if expect == 1 else a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4) + a256(8 * 8))
 
 
 def test_selector_is_shape_only_and_bounded():
