@@ -78,12 +78,20 @@ typedef struct {
     int64_t pool_pages;        /* >= 1: pages in kv_pool                            */
 } smla_shape;
 
+/* Where the split partials are merged (smla_plan.merge). */
+#define SMLA_MERGE_AUTO 0      /* in a plan passed in: let the selector choose; in a plan
+                                  returned: nothing to merge (nsplit = 1)                  */
+#define SMLA_MERGE_IN_KERNEL 1 /* the last split of each request to finish merges them, in
+                                  the same launch                                          */
+#define SMLA_MERGE_SEPARATE 2  /* a second launch: the combine kernel                      */
+
 /* Launch plan.  Zero fields mean "choose automatically". */
 typedef struct {
     int32_t nsplit;       /* top-k splits per request (1..16); 1 = no partials, no merge  */
     int32_t tile_tokens;  /* tokens per pipeline tile (only 32 is supported)              */
     int32_t heads_per_wg; /* query heads per workgroup (only 64 is supported)             */
     int32_t wg_per_cu;    /* resident workgroups per compute unit assumed by the selector */
+    int32_t merge;        /* SMLA_MERGE_*                                                 */
 } smla_plan;
 
 /*
@@ -133,10 +141,12 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *                        and every successful call leaves the counters at zero again.
  *                        Calls that share a workspace must not overlap in time.
  *   stream     hipStream_t (NULL = default stream)
- * The work runs as one kernel launch: each (request, split) workgroup writes
- * its partial result, and the last split of a request to finish merges them
- * (the log-sum-exp combine of "The 64-Block Barrier", section "The Split-K
- * Prescription", fused into the same launch).
+ * With nsplit = 1 the work is one kernel launch.  Otherwise each (request,
+ * split) workgroup writes its partial result and the partials are merged by
+ * the log-sum-exp combine of "The 64-Block Barrier", section "The Split-K
+ * Prescription": either by the last split of each request to finish, in the
+ * same launch (SMLA_MERGE_IN_KERNEL), or by the combine kernel launched right
+ * after on the same stream (SMLA_MERGE_SEPARATE), as the plan says.
  * Returns SMLA_OK or a negative SMLA_ERR_* code.
  */
 int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_table,

@@ -31,6 +31,10 @@ ERR_WORKSPACE = -3
 ERR_PLAN = -4
 ERR_HIP = -5
 
+MERGE_AUTO = 0
+MERGE_IN_KERNEL = 1
+MERGE_SEPARATE = 2
+
 
 class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
@@ -41,7 +45,7 @@ class Shape(ctypes.Structure):
 
 class Plan(ctypes.Structure):
     _fields_ = [("nsplit", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
-                ("heads_per_wg", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32)]
+                ("heads_per_wg", ctypes.c_int32), ("wg_per_cu", ctypes.c_int32), ("merge", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: int(getattr(self, f)) for f, _ in self._fields_}
@@ -107,8 +111,9 @@ def _plan_arg(plan):
         return ctypes.byref(plan)
     if isinstance(plan, dict):
         return ctypes.byref(Plan(int(plan.get("nsplit", 0)), int(plan.get("tile_tokens", 0)),
-                                 int(plan.get("heads_per_wg", 0)), int(plan.get("wg_per_cu", 0))))
-    return ctypes.byref(Plan(int(plan), 0, 0, 0))     # an int = forced nsplit
+                                 int(plan.get("heads_per_wg", 0)), int(plan.get("wg_per_cu", 0)),
+                                 int(plan.get("merge", 0))))
+    return ctypes.byref(Plan(int(plan), 0, 0, 0, 0))     # an int = forced nsplit
 
 
 def plan_for(shape: Shape, plan=None):

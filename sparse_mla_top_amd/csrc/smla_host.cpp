@@ -59,22 +59,33 @@ size_t workspace_for(int B, int nsplit) {
   return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * 2 * sizeof(uint32_t));
 }
 
-// Estimated time (us) of one call with `nsplit` splits on `cus` compute units.
-// One workgroup is resident per CU (its LDS tiles take most of the 160 KiB),
-// so B * nsplit workgroups run in ceil(B*nsplit / cus) dispatch rounds, each
-// as long as the longest split (chunk tiles of 32 tokens).  Splitting also
-// writes and re-reads a normalised fp32 partial per (request, split, head),
-// merged by the last split of each request to finish.  The constants are
-// fitted to MI355X timings of the fused kernel on cold caches.
-double est_time_us(int B, int nsplit, int chunk_tiles, int cus) {
-  const double t_start = 9.3;     // launch, translation and first-gather latency per workgroup
-  const double t_tile = 1.27;     // one 32-token tile for 64 heads on one CU
-  const double t_merge0 = 6.3;    // arrival, coherent partial write/read latency of the merge
-  const double t_merge_split = 1.6;  // per partial read by the merging workgroup
+// Estimated time (us) of one call with `nsplit` splits on `cus` compute units
+// and the given merge placement.  One workgroup is resident per CU (its LDS
+// tiles take most of the 160 KiB), so B * nsplit workgroups run in
+// ceil(B*nsplit / cus) dispatch rounds, each as long as the longest split
+// (chunk tiles of 32 tokens).  Splitting adds the merge: in the kernel, one
+// workgroup per request reads every partial (bounded by one CU's memory
+// parallelism); as a separate launch, a launch gap plus a short,
+// device-wide read.  The constants are fitted to MI355X timings on cold
+// caches.
+double est_time_us(int B, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
+  const double t_start = 9.3;        // launch, translation and first-gather latency per workgroup
+  const double t_tile = 1.27;        // one 32-token tile for 64 heads on one CU
+  const double us_per_mb = 0.09;     // gathered rows and per-split Q reads, device-wide
+  const double t_fused0 = 5.5, t_fused_split = 1.3;   // in-kernel merge: one workgroup reads every partial
+  const double t_sep0 = 3.5, t_sep_round = 1.3;       // combine launch: gap, lse, one round per 4 partials
+  const double us_per_mb_part = 0.095;                // partial bytes written and read back
+  const double mb = 1.0 / (1 << 20);
   const int grid = B * nsplit;
   const int rounds = (grid + cus - 1) / cus;
-  double t = rounds * (t_start + chunk_tiles * t_tile);
-  if (nsplit > 1) t += t_merge0 + t_merge_split * nsplit;
+  double t = rounds * (t_start + chunk_tiles * t_tile) +
+             us_per_mb * mb * (double)B * ((double)kTopk * row_bytes + (double)nsplit * kHeads * kDqk * 2);
+  if (nsplit > 1) {
+    if (merge == SMLA_MERGE_IN_KERNEL)
+      t += t_fused0 + t_fused_split * nsplit;
+    else
+      t += t_sep0 + t_sep_round * ((nsplit + 3) / 4) + us_per_mb_part * mb * 2.0 * grid * kHeads * kDv * 4.0;
+  }
   return t;
 }
 
@@ -108,30 +119,38 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!out || !workspace_bytes || num_cus < 1) return SMLA_ERR_INVALID_ARG;
-  smla_plan p = {0, kTile, kHeads, 1};
+  smla_plan p = {0, kTile, kHeads, 1, SMLA_MERGE_AUTO};
   if (ov) {
     if (ov->nsplit < 0 || ov->nsplit > kTiles) return SMLA_ERR_PLAN;
     if (ov->tile_tokens != 0 && ov->tile_tokens != kTile) return SMLA_ERR_PLAN;
     if (ov->heads_per_wg != 0 && ov->heads_per_wg != kHeads) return SMLA_ERR_PLAN;
     if (ov->wg_per_cu < 0 || ov->wg_per_cu > 1) return SMLA_ERR_PLAN;
+    if (ov->merge < SMLA_MERGE_AUTO || ov->merge > SMLA_MERGE_SEPARATE) return SMLA_ERR_PLAN;
     p.nsplit = ov->nsplit;
+    p.merge = ov->merge;
   }
   const int B = shape->batch;
   const int slots = num_cus * p.wg_per_cu;
-  if (p.nsplit == 0) {
-    double best = INFINITY;
-    int best_ns = 1;
-    for (int ns = 1; ns <= kTiles; ++ns) {
-      const int chunk = (kTiles + ns - 1) / ns;
-      if ((kTiles + chunk - 1) / chunk != ns) continue;   // only split counts with no empty split
-      const double t = est_time_us(B > 0 ? B : 1, ns, chunk, slots);
-      if (t < best - 1e-9) { best = t; best_ns = ns; }
-    }
-    p.nsplit = best_ns;
+  // a forced split count is normalised to whole tiles with no empty split
+  int forced = 0;
+  if (p.nsplit != 0) {
+    const int c = (kTiles + p.nsplit - 1) / p.nsplit;
+    forced = (kTiles + c - 1) / c;
   }
-  // normalise: chunk of whole tiles, no empty trailing split
-  const int chunk = (kTiles + p.nsplit - 1) / p.nsplit;
-  p.nsplit = (kTiles + chunk - 1) / chunk;
+  double best = INFINITY;
+  int best_ns = 1, best_merge = SMLA_MERGE_SEPARATE;
+  for (int ns = 1; ns <= kTiles; ++ns) {
+    const int chunk = (kTiles + ns - 1) / ns;
+    if ((kTiles + chunk - 1) / chunk != ns) continue;   // only split counts with no empty split
+    if (forced != 0 && ns != forced) continue;
+    for (int m = SMLA_MERGE_IN_KERNEL; m <= SMLA_MERGE_SEPARATE; ++m) {
+      if (p.merge != SMLA_MERGE_AUTO && m != p.merge) continue;
+      const double t = est_time_us(B > 0 ? B : 1, ns, chunk, slots, m, smla_row_bytes(shape->kv_format));
+      if (t < best - 1e-9) { best = t; best_ns = ns; best_merge = m; }
+    }
+  }
+  p.nsplit = best_ns;
+  p.merge = p.nsplit > 1 ? best_merge : SMLA_MERGE_AUTO;
   *out = p;
   *workspace_bytes = workspace_for(B, p.nsplit);
   return SMLA_OK;
@@ -152,6 +171,7 @@ struct Prepared {
   CombineArgs combine;
   int B = 0;
   int nsplit = 1;
+  int merge = SMLA_MERGE_AUTO;
   int fmt = 0;
 };
 
@@ -200,6 +220,7 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   c.lse = lse;
   pr->B = B;
   pr->nsplit = plan.nsplit;
+  pr->merge = plan.merge;
   pr->fmt = shape->kv_format;
   return SMLA_OK;
 }
@@ -212,6 +233,12 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
   int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
+  if (pr.nsplit > 1 && pr.merge == SMLA_MERGE_SEPARATE) {
+    pr.split.counters = nullptr;       // partials only; the combine launch merges them
+    if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_combine(pr.combine, pr.B, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+    return SMLA_OK;
+  }
   // one launch: the last split of each request merges the partials
   if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;

@@ -78,17 +78,44 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       : "m0");
 }
 
-// Issue the direct-to-LDS loads of one tile (kTile rows).  Row r of the tile
-// lands at lds + r * kRow; its 16-byte chunk c comes from the row's address
-// (the zero row when the slot is masked; bit 0 of the address marks that).
-// Issuing wave v (0..3) takes load instructions v, v+4, ... of the tile; the
-// count per wave is DmaCount<FMT>::of(v).
+// Layout of a tile (kTile = 32 rows of kRow / 16 chunks of 16 bytes) in LDS.
+// Chunks go in groups of four; the 16 rows x 4 chunks of a row half and a
+// chunk group form one 1 KB block, in which the 16 rows of each chunk are
+// contiguous:
+//   slot(row, chunk) = ((chunk / 4) * 2 + row / 16) * 64 + (chunk % 4) * 16 + row % 16
+// A ds_read_b128 runs at the full 256 B/clk only when each 16 consecutive
+// lanes read one contiguous 256-byte span; the QK operand reads (16 lanes =
+// 16 rows of one chunk) do here, where rows 656 bytes apart conflict two-way.
+// Each direct-to-LDS instruction fills one block (16 rows x 64 bytes).  A
+// 41-chunk fp8 row leaves one chunk after its 10 groups: it takes a 32-slot
+// tail, slot 1280 + row.
+template <int FMT> struct TileLayout {
+  static constexpr int kChunksRow = RowFmt<FMT>::kRow / 16;   // 41 (fp8) or 72 (bf16)
+  static constexpr int kGroups = kChunksRow / 4;
+  static constexpr int kTail = kGroups * 128;                 // first slot after the groups
+  static constexpr int kSlots = kTile * kChunksRow;
+  __device__ static constexpr uint32_t off(int row, int chunk) {   // byte offset in the tile
+    return 16u * (uint32_t)(chunk < 4 * kGroups ? ((chunk >> 2) * 2 + (row >> 4)) * 64 + (chunk & 3) * 16 + (row & 15)
+                                                : kTail + (chunk - 4 * kGroups) * kTile + row);
+  }
+  __device__ static constexpr int row_of(int slot) {
+    return slot < kTail ? 16 * ((slot >> 6) & 1) + (slot & 15) : (slot - kTail) % kTile;
+  }
+  __device__ static constexpr int chunk_of(int slot) {
+    return slot < kTail ? 4 * (slot >> 7) + ((slot >> 4) & 3) : 4 * kGroups + (slot - kTail) / kTile;
+  }
+};
+
+// Issue the direct-to-LDS loads of one tile: slot s of the layout above takes
+// chunk chunk_of(s) of row row_of(s), read from that row's address (the zero
+// row when the slot is masked; bit 0 of the address marks that).  Issuing
+// wave v (0..3) takes load instructions v, v+4, ... of the tile; the count
+// per wave is DmaCount<FMT>::of(v).
 template <int FMT>
 __device__ __forceinline__ void issue_tile(const uint64_t LDS_AS* rowaddr_s, int tok0,
                                            uint8_t LDS_AS* lds, int v, int lane) {
-  constexpr int kRow = RowFmt<FMT>::kRow;
-  constexpr int kChunksRow = kRow / 16;
-  constexpr int kChunks = kTile * kChunksRow;
+  using TL = TileLayout<FMT>;
+  constexpr int kChunks = TL::kSlots;
   constexpr int kInstr = (kChunks + 63) / 64;
   constexpr int kPerWave = (kInstr + 3) / 4;
   // all source addresses first (one LDS round trip), then the loads
@@ -97,9 +124,7 @@ __device__ __forceinline__ void issue_tile(const uint64_t LDS_AS* rowaddr_s, int
   for (int q = 0; q < kPerWave; ++q) {
     const int c = (v + 4 * q) * 64 + lane;
     const int cc = c < kChunks ? c : 0;
-    const int r = cc / kChunksRow;
-    const int off = (cc - r * kChunksRow) * 16;
-    src[q] = (const void*)(uintptr_t)((rowaddr_s[tok0 + r] & ~1ull) + off);
+    src[q] = (const void*)(uintptr_t)((rowaddr_s[tok0 + TL::row_of(cc)] & ~1ull) + 16 * TL::chunk_of(cc));
   }
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
@@ -238,94 +263,23 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 // M = max_s lse_s, lse = M + ln sum_s w_s; all splits empty -> out 0, lse -inf.
 // Thread t owns head t/8 and dims 64(t%8) .. +63.
 // Softmax weights of the nsplit partials of one head, written to
-// wt[sp * kHeads] (normalised: they sum to 1), and the merged lse:
+// wt[sp * stride] (normalised: they sum to 1), and the merged lse:
 //   w_s = exp(lse_s - M) / sum_r exp(lse_r - M),  M = max_s lse_s,
 //   lse = M + ln sum_r exp(lse_r - M);  every split empty -> w = 0, lse = -inf.
 // Both merge paths call this, so they round identically.
 template <class LseOf>
-__device__ __forceinline__ float split_weights(int nsplit, LseOf lse_of, float* wt) {
+__device__ __forceinline__ float split_weights(int nsplit, LseOf lse_of, float* wt, int stride = kHeads) {
   float M = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, lse_of(sp));
   float wsum = 0.f;
   for (int sp = 0; sp < nsplit; ++sp) {
     const float e = M == -INFINITY ? 0.f : __expf(lse_of(sp) - M);
-    wt[sp * kHeads] = e;
+    wt[sp * stride] = e;
     wsum += e;
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) wt[sp * kHeads] *= inv;
+  for (int sp = 0; sp < nsplit; ++sp) wt[sp * stride] *= inv;
   return wsum > 0.f ? M + __logf(wsum) : -INFINITY;
-}
-
-// Merge the nsplit partials of request b (512 threads, weights already in
-// wt[sp * kHeads + head]): out = sum_s w_s O_s, accumulated in split order.
-// run_of(sp, byte_offset) returns the float4 of partial sp at that offset of
-// its 128 KB block.  Wave w takes latent slice vb = w/2 and 32-dim blocks
-// 2(w%2) + 0..1, i.e. 16 runs; the runs of two splits are loaded together.
-template <class RunOf>
-__device__ __forceinline__ void merge_runs(int nsplit, int b, uint16_t* __restrict__ out, const float* wt,
-                                           RunOf run_of) {
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
-  const int vb = wave >> 1, db0 = 2 * (wave & 1);
-  f32x4 acc[2][4][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) acc[i][j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < nsplit; sp += 2) {
-    const bool two = sp + 1 < nsplit;
-    f32x4 v[2][2][4][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            v[u][i][j][hb] = (u == 0 || two) ? run_of(sp + u, part_run_offset(vb, db0 + i, j, hb, lane))
-                                             : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u == 1 && !two) break;
-      const float w0 = wt[(sp + u) * kHeads + l32], w1 = wt[(sp + u) * kHeads + 32 + l32];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j][0] += w0 * v[u][i][j][0];
-          acc[i][j][1] += w1 * v[u][i][j][1];
-        }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const f32x4 x = acc[i][j][hb];
-        const uint32_t lo = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
-        uint16_t* orow = out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 32 * (db0 + i) + 8 * j + 4 * kg;
-        *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
-      }
-}
-
-// Weights of request b's splits into wt (16 x 64 floats of LDS) and the merged
-// lse into lse[b, :] (512 threads).  lse_of(sp, h) gives split sp's lse of
-// head h; all of them are fetched in one parallel pass first.
-template <class LseOf>
-__device__ __forceinline__ void merge_weights(int nsplit, int b, float* __restrict__ lse, float* wt, LseOf lse_of) {
-  for (int i = threadIdx.x; i < nsplit * kHeads; i += kThreads) wt[i] = lse_of(i >> 6, i & (kHeads - 1));
-  lds_barrier();
-  const int t = threadIdx.x;
-  if (t < kHeads)    // in place: column t is read before it is overwritten
-    lse[(int64_t)b * kHeads + t] = split_weights(nsplit, [&](int sp) { return wt[sp * kHeads + t]; }, wt + t);
-  lds_barrier();
 }
 
 __device__ __forceinline__ f32x4 load_run(const float* part_o, int64_t block, uint32_t off) {
@@ -333,21 +287,10 @@ __device__ __forceinline__ f32x4 load_run(const float* part_o, int64_t block, ui
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
 }
 
-// Merge the nsplit partials of request b from the workspace (512 threads).
-// wt is 16 x 64 floats of LDS.
-__device__ __forceinline__ void merge_request(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                              int nsplit, int b, uint16_t* __restrict__ out, float* __restrict__ lse,
-                                              float* wt) {
-  const float* ls = part_lse + (int64_t)b * nsplit * kHeads;
-  merge_weights(nsplit, b, lse, wt, [&](int sp, int h) { return load_agent(ls + sp * kHeads + h); });
-  merge_runs(nsplit, b, out, wt,
-             [&](int sp, uint32_t off) { return load_run(part_o, (int64_t)b * nsplit + sp, off); });
-}
-
 // The fused merge of request b by its last split `own` (512 threads).  Its
 // own partial is in LDS (`own_part`, workspace-block layout) with its lse in
 // own_lse[h]; the other nsplit - 1 partials and lses are in the workspace.
-// Same weights and the same split-ordered accumulation as merge_request, but
+// Same weights and the same split-ordered accumulation as the combine kernel;
 // the lse loads and the first partial loads go out together, and each round
 // loads two partials other than the own one: one memory round trip when
 // nsplit <= 3.
@@ -472,6 +415,7 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   constexpr int kRow = RowFmt<FMT>::kRow;
   constexpr int kNbuf = RowFmt<FMT>::kNbuf;
+  using TL = TileLayout<FMT>;
   constexpr int kTileBytes = kTile * kRow;
   // One LDS block: the tile ring, then P^T.  A merging workgroup reuses its
   // first 128 KB for its own partial output.
@@ -567,7 +511,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // at least 4 buffers (fp8 rows: 6; bf16 rows fit only 3 and run unpipelined,
   // tile k scored and finished in iteration k).
   constexpr bool kPipe = kNbuf >= 4;
-  const int npre = min(kAhead, ntiles);
+  // Only the tiles the first iteration needs go out before it: every
+  // workgroup starts at once, and a deeper first burst would delay everyone's
+  // first tile behind the others' later ones.  The rest follow at its top.
+  const int npre = min(kPipe ? 2 : kAhead, ntiles);
   if (!qk_role)
     for (int tt = 0; tt < npre; ++tt)
       issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile,
@@ -577,8 +524,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // barrier publishes it; then they issue tile k + kAhead.
   auto iteration_head = [&](int k) {
     const int need = kPipe ? k + 1 : k;   // the tile the QK waves start in iteration k
+    const int issued = k == 0 ? npre : min(ntiles, k + kAhead);   // tiles issued so far
     if (!qk_role && need < ntiles) {
-      const int after = min(ntiles, k + kAhead) - need - 1;   // tiles issued after it
+      const int after = issued - need - 1;                    // tiles issued after it
       if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(after);
       else wait_tiles<DmaCount<FMT>::of(3)>(after);
     } else if (!qk_role && k < ntiles) {
@@ -586,9 +534,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       else wait_tiles<DmaCount<FMT>::of(3)>(0);
     }
     lds_barrier();
-    if (!qk_role && k + kAhead < ntiles)
-      issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, (k + kAhead) * kTile,
-                      (uint8_t LDS_AS*)(tiles + ((k + kAhead) % kNbuf) * kTileBytes), vwave, lane);
+    if (!qk_role) {
+      // tile k + kAhead (at k = 0 also the ones the prefetch left out)
+      for (int tt = k == 0 ? npre : k + kAhead; tt <= k + kAhead && tt < ntiles; ++tt)
+        issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile,
+                        (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), vwave, lane);
+    }
   };
 
   if (qk_role) {
@@ -660,11 +611,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         // one 16-token half at a time (18 operand registers of 4 each)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const uint8_t* krow = tb + (16 * m + c16) * kRow;
+          const int row = 16 * m + c16;
           f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+          // k-slot group g of 32-dim step c: dims 32c + 8g .. +7 = chunk 4c + g
 #pragma unroll
           for (int c = 0; c < 18; ++c)
-            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(krow + 2 * (32 * c + 8 * g)),
+            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(tb + TL::off(row, 4 * c + g)),
                                                         qb[c], sm, 0, 0, 0);
           r.sm[m] = sm;
         }
@@ -673,16 +625,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         bf16x8 kr[2][2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const uint8_t* krow = tb + (16 * m + c16) * kRow;
+          const int row = 16 * m + c16;
+          // codes 128blk + 32g .. +31 = chunks 8blk + 2g, +1
 #pragma unroll
           for (int blk = 0; blk < 4; ++blk) {
-            const i32x4 k0 = *reinterpret_cast<const i32x4*>(krow + 128 * blk + 32 * g);
-            const i32x4 k1 = *reinterpret_cast<const i32x4*>(krow + 128 * blk + 32 * g + 16);
+            const i32x4 k0 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g));
+            const i32x4 k1 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g + 1));
             ka[m][blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
           }
+          // rope dims 32c + 8g .. +7 sit at byte 528 + 2 (32c + 8g): chunk 33 + 4c + g
 #pragma unroll
           for (int c = 0; c < 2; ++c)
-            kr[m][c] = *reinterpret_cast<const bf16x8*>(krow + kDl + 16 + 2 * (32 * c + 8 * g));
+            kr[m][c] = *reinterpret_cast<const bf16x8*>(tb + TL::off(row, 33 + 4 * c + g));
         }
         // independent MFMA chains per half: hi of every block, rope, then lo
 #pragma unroll
@@ -714,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         if constexpr (FMT == kFmtFp8) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float4 sv = *reinterpret_cast<const float4*>(tb + (16 * m + 4 * g + i) * kRow + kDl);
+            const float4 sv = *reinterpret_cast<const float4*>(tb + TL::off(16 * m + 4 * g + i, kDl / 16));
             sm[i] += r.acc[m][0][i] * sv.x + r.acc[m][1][i] * sv.y + r.acc[m][2][i] * sv.z + r.acc[m][3][i] * sv.w;
           }
         }
@@ -850,7 +804,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         float sc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          sc[i] = (FMT == kFmtFp8) ? *reinterpret_cast<const float*>(tb + (16 * kh + 8 * kg + i) * kRow + kDl + 4 * vb)
+          sc[i] = (FMT == kFmtFp8) ? *reinterpret_cast<const float*>(tb + TL::off(16 * kh + 8 * kg + i, kDl / 16) + 4 * vb)
                                    : 1.0f;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -881,16 +835,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
             // 16-lane group gg reads tokens 16kh + 8(gg>>1) + 0..7 x dims
             // 32db + 16(gg&1) + 0..15; source lane (2r + half) supplies 8 bytes of row r
             const int gg = lane >> 4, r = c16 >> 1, half = c16 & 1;
-            const uint8_t* src = tb + (16 * kh + 8 * (gg >> 1) + r) * kRow + 128 * vb + 32 * db + 16 * (gg & 1) + 8 * half;
+            const uint8_t* src = tb + TL::off(16 * kh + 8 * (gg >> 1) + r, 8 * vb + 2 * db + (gg & 1)) + 8 * half;
             const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
             va = fp8x8_to_bf16((uint64_t)(uint32_t)raw[0] | ((uint64_t)(uint32_t)raw[1] << 32));
           } else {
             // two 4-row reads per group: rows 16kh + 8(gg>>1) + 0..3 and + 4..7;
             // source lane (4r + q) supplies 4 elements of row r
             const int gg = lane >> 4, r = c16 >> 2, q = c16 & 3;
-            const uint8_t* src = tb + (16 * kh + 8 * (gg >> 1) + r) * kRow + 2 * (128 * vb + 32 * db + 16 * (gg & 1)) + 8 * q;
-            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)src);
-            const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(src + 4 * kRow));
+            // dims 128vb + 32db + 16(gg&1) + 4q .. +3: chunk 16vb + 4db + 2(gg&1) + q/2, byte 8(q&1)
+            const int row = 16 * kh + 8 * (gg >> 1) + r, chunk = 16 * vb + 4 * db + 2 * (gg & 1) + (q >> 1);
+            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(tb + TL::off(row, chunk) + 8 * (q & 1)));
+            const i16x4 r1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(tb + TL::off(row + 4, chunk) + 8 * (q & 1)));
             // whole-vector bit casts: element-wise short -> __bf16 casts of this
             // result were mis-lowered (the upper dword was dropped)
             const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
@@ -943,7 +899,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           for (int jj = 0; jj < 4; ++jj) {
             const f32x4 v = {o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb],
                              o[db][hb][4 * jj + 2] * inv[hb], o[db][hb][4 * jj + 3] * inv[hb]};
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, kSc1);
+            if (fused)   // read back in this launch, possibly on another XCD
+              __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, kSc1);
+            else         // read by the combine launch
+              __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, 0);
           }
     } else {
       // last split of the request: its own partial goes to LDS, in the
@@ -989,11 +948,66 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Combine as a launch of its own: one 512-thread workgroup per request runs
-// the same merge as the fused path, so both give identical bits.
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float wt[16 * kHeads];
-  merge_request(a.part_o, a.part_lse, a.nsplit, blockIdx.x, a.out, a.lse, wt);
+// Combine as a launch of its own, spread over the device: one 256-thread
+// workgroup per (request, latent slice vb, 32-head block hb); wave w merges
+// the four runs (vb, db = w, jj, hb).  Weights come from split_weights and the
+// runs are accumulated in split order, exactly as the fused merge does, so
+// both give identical bits.
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
+  __shared__ float wt[16 * 32];
+  const int b = blockIdx.x >> 3, vb = (blockIdx.x >> 1) & 3, hb = blockIdx.x & 1;
+  const int t = threadIdx.x, db = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
+  const int ns = a.nsplit;
+  const float* ls = a.part_lse + (int64_t)b * ns * kHeads + 32 * hb;
+  // the lse loads (two per thread at most) and the first four partials go
+  // out together: the weights are computed while the runs are in flight
+  float lv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = t + u * kCombineThreads;
+    lv[u] = i < ns * 32 ? load_agent(ls + (i >> 5) * kHeads + (i & 31)) : 0.f;
+  }
+  f32x4 v[4][4];
+  auto issue = [&](int sp) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[u][j] = sp + u < ns ? load_run(a.part_o, (int64_t)b * ns + sp + u, part_run_offset(vb, db, j, hb, lane))
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  issue(0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (t + u * kCombineThreads < ns * 32) wt[t + u * kCombineThreads] = lv[u];
+  __syncthreads();
+  if (t < 32) {   // in place, column t: the lse of head 32hb + t
+    const float l = split_weights(ns, [&](int sp) { return wt[sp * 32 + t]; }, wt + t, 32);
+    if (vb == 0) a.lse[(int64_t)b * kHeads + 32 * hb + t] = l;
+  }
+  __syncthreads();
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < ns; sp += 4) {
+    if (sp > 0) issue(sp);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (sp + u >= ns) break;
+      const float w = wt[(sp + u) * 32 + l32];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += w * v[u][j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 x = acc[j];
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+    uint16_t* orow = a.out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 32 * db + 8 * j + 4 * kg;
+    *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1030,7 +1044,7 @@ hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t st
 }
 
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(B), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(B * 8), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -73,7 +73,8 @@ def test_null_pointers_and_bad_scale():
 
 def test_plan_overrides_validated():
     s = _shape()
-    for bad in ({"nsplit": 17}, {"nsplit": -1}, {"tile_tokens": 16}, {"heads_per_wg": 32}, {"wg_per_cu": 3}):
+    for bad in ({"nsplit": 17}, {"nsplit": -1}, {"tile_tokens": 16}, {"heads_per_wg": 32}, {"wg_per_cu": 3},
+                {"merge": 3}, {"merge": -1}):
         with pytest.raises(smla.SmlaError) as e:
             smla.plan_for_cus(s, 256, bad)
         assert e.value.code == smla.ERR_PLAN
@@ -95,6 +96,8 @@ def test_selector_is_shape_only_and_bounded():
     for B in (1, 8, 16, 32, 48, 64, 80, 88, 96, 300):
         p, ws = smla.plan_for_cus(_shape(batch=B), 256)
         assert 1 <= p.nsplit <= 16
+        # a merge placement exactly when there is something to merge
+        assert (p.merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE)) == (p.nsplit > 1)
         p2, ws2 = smla.plan_for_cus(_shape(batch=B), 256)
         assert p.as_dict() == p2.as_dict() and ws == ws2
     # with many requests the grid already fills the device: no split needed
@@ -140,3 +143,12 @@ def test_pages_worked_grid_numbers():
     assert round(old["blocks"] / old["sms"], 2) == old["occupancy"]
     sk = g["split_k_target"]
     assert sk["B"] * sk["H"] * sk["nsplit"] == sk["blocks"]
+
+
+@pytest.mark.parametrize("merge", [1, 2])
+def test_forced_merge_placement_is_kept(merge):
+    p, ws = smla.plan_for_cus(_shape(batch=8), 256, {"nsplit": 4, "merge": merge})
+    assert (p.nsplit, p.merge) == (4, merge)
+    # nothing to merge with one split
+    p, ws = smla.plan_for_cus(_shape(batch=8), 256, {"nsplit": 1, "merge": merge})
+    assert (p.nsplit, p.merge, ws) == (1, 0, 0)

@@ -82,7 +82,8 @@ def test_decode_b1_in_fp8_format():
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
 def test_decode_forced_nsplit(nsplit, fmt):
     w = W.build("nsplit", 930, fmt, 6, [65536, 4096, 700, 513, 300, 131072], fmt, "uniform")
-    _check(w, plan=nsplit, what=f"forced nsplit={nsplit} fmt={fmt}")
+    for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+        _check(w, plan={"nsplit": nsplit, "merge": merge}, what=f"forced nsplit={nsplit} merge={merge} fmt={fmt}")
 
 
 def test_nsplit_results_agree():
@@ -173,20 +174,31 @@ def test_empty_batch_and_errors():
 
 
 def test_split_and_combine_stages_equal_decode():
+    """In-kernel merge, separate-launch merge and the two stages called one by
+    one give identical bits (same weights, same split-ordered sums)."""
     w = W.make(2)
     d = upload(w)
     shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages)
-    for ns in (1, 4):
+    for ns in (1, 3, 4, 16):
         plan, ws_bytes = smla.plan_for(shape, ns)
         ws = smla.new_workspace(ws_bytes)
-        o1 = torch.empty((w.B, 64, 512), dtype=torch.bfloat16, device="cuda")
-        l1 = torch.empty((w.B, 64), dtype=torch.float32, device="cuda")
-        o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
-        assert smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o1, l1, shape, ns, ws) == 0
+        res = []
+        for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+            o = torch.empty((w.B, 64, 512), dtype=torch.bfloat16, device="cuda")
+            l = torch.empty((w.B, 64), dtype=torch.float32, device="cuda")
+            pl = {"nsplit": ns, "merge": merge}
+            assert smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l, shape, pl, ws) == 0
+            res.append((o, l))
+        o2, l2 = torch.empty_like(res[0][0]), torch.empty_like(res[0][1])
         assert smla.split_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o2, l2, shape, ns, ws) == 0
         assert smla.combine_raw(shape, ns, ws, o2, l2) == 0
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        res.append((o2, l2))
+        for o, l in res[1:]:
+            assert torch.equal(res[0][0], o) and torch.equal(res[0][1], l), f"nsplit={ns}"
+        if ns == 4:
+            ref_o, ref_l = oracle.decode_workload(w)
+            assert_parity(res[1][0], res[1][1], ref_o, ref_l, "separate merge nsplit=4")
 
 
 def test_fused_merge_repeated_calls_share_workspace():
@@ -198,7 +210,8 @@ def test_fused_merge_repeated_calls_share_workspace():
         pool = w.host_pool()
         d = upload(w)
         out, lse = smla.decode(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, kv_format=d.kv_format,
-                               pool_pages=d.pool_pages, plan=ns, workspace=ws)
+                               pool_pages=d.pool_pages, plan={"nsplit": ns, "merge": smla.MERGE_IN_KERNEL},
+                               workspace=ws)
         torch.cuda.synchronize()
         ref_o, ref_l = oracle.decode_workload(w, pool=pool)
         assert_parity(out, lse, ref_o, ref_l, f"fused merge call {it} {w.name} nsplit={ns}")
@@ -212,7 +225,7 @@ def test_workspace_init_recovers_dirty_counters():
     ws = torch.full((ws_bytes,), 0x5A, dtype=torch.uint8, device="cuda")   # garbage everywhere
     smla.workspace_init(ws)
     out, lse = smla.decode(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, kv_format=d.kv_format,
-                           pool_pages=d.pool_pages, plan=4, workspace=ws)
+                           pool_pages=d.pool_pages, plan={"nsplit": 4, "merge": smla.MERGE_IN_KERNEL}, workspace=ws)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.decode_workload(w)
     assert_parity(out, lse, ref_o, ref_l, "after workspace_init")
