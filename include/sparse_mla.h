@@ -89,7 +89,8 @@ typedef struct {
 typedef struct {
     int32_t nsplit;       /* top-k splits per request (1..16); 1 = no partials, no merge  */
     int32_t tile_tokens;  /* tokens per pipeline tile (only 32 is supported)              */
-    int32_t heads_per_wg; /* query heads per workgroup (only 64 is supported)             */
+    int32_t heads_per_wg; /* query heads per workgroup (only 32 is supported: two head  */
+                          /* groups per request gather the same rows)                  */
     int32_t wg_per_cu;    /* resident workgroups per compute unit assumed by the selector */
     int32_t merge;        /* SMLA_MERGE_*                                                 */
 } smla_plan;

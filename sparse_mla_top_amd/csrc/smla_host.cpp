@@ -50,33 +50,34 @@ int check_shape(const smla_shape* s) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout (nsplit > 1): fp32 partial outputs [B, nsplit, 64, 512],
-// fp32 partial lse [B, nsplit, 64], uint32 counters [B][2] (arrival tickets,
-// finished partial writes); each region starts at a 256-byte boundary.
+// fp32 partial lse [B, nsplit, 64], uint32 counters [B][head group][2]
+// (arrival tickets, finished partial writes); each region starts at a
+// 256-byte boundary.
 size_t ws_part_o_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * kDv * sizeof(float)); }
 size_t ws_part_lse_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * sizeof(float)); }
 size_t workspace_for(int B, int nsplit) {
   if (nsplit <= 1 || B == 0) return 0;
-  return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * 2 * sizeof(uint32_t));
+  return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * kHeadGroups * 2 * sizeof(uint32_t));
 }
 
 // Estimated time (us) of one call with `nsplit` splits on `cus` compute units
 // and the given merge placement.  One workgroup is resident per CU (its LDS
-// tiles take most of the 160 KiB), so B * nsplit workgroups run in
-// ceil(B*nsplit / cus) dispatch rounds, each as long as the longest split
-// (chunk tiles of 32 tokens).  Splitting adds the merge: in the kernel, one
+// tiles take most of the 160 KiB), so the B * 2 * nsplit workgroups (two head
+// groups per request) run in ceil(B*2*nsplit / cus) dispatch rounds, each as
+// long as the longest split (chunk tiles of 32 tokens).  Splitting adds the merge: in the kernel, one
 // workgroup per request reads every partial (bounded by one CU's memory
 // parallelism); as a separate launch, a launch gap plus a short,
 // device-wide read.  The constants are fitted to MI355X timings on cold
 // caches.
 double est_time_us(int B, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
-  const double t_start = 9.3;        // launch, translation and first-gather latency per workgroup
-  const double t_tile = 1.27;        // one 32-token tile for 64 heads on one CU
+  const double t_start = 8.0;        // launch, translation and first-gather latency per workgroup
+  const double t_tile = 1.0;         // one 32-token tile for 32 heads on one CU
   const double us_per_mb = 0.09;     // gathered rows and per-split Q reads, device-wide
-  const double t_fused0 = 5.5, t_fused_split = 1.3;   // in-kernel merge: one workgroup reads every partial
-  const double t_sep0 = 3.5, t_sep_round = 1.3;       // combine launch: gap, lse, one round per 4 partials
-  const double us_per_mb_part = 0.095;                // partial bytes written and read back
+  const double t_fused0 = 4.5, t_fused_split = 0.6;   // in-kernel merge: one workgroup reads every partial
+  const double t_sep0 = 3.0, t_sep_split = 0.3;       // combine launch: gap, lse, partial rounds
+  const double us_per_mb_part = 0.2;                  // partial bytes written and read back
   const double mb = 1.0 / (1 << 20);
-  const int grid = B * nsplit;
+  const int grid = B * kHeadGroups * nsplit;
   const int rounds = (grid + cus - 1) / cus;
   double t = rounds * (t_start + chunk_tiles * t_tile) +
              us_per_mb * mb * (double)B * ((double)kTopk * row_bytes + (double)nsplit * kHeads * kDqk * 2);
@@ -84,7 +85,7 @@ double est_time_us(int B, int nsplit, int chunk_tiles, int cus, int merge, int r
     if (merge == SMLA_MERGE_IN_KERNEL)
       t += t_fused0 + t_fused_split * nsplit;
     else
-      t += t_sep0 + t_sep_round * ((nsplit + 3) / 4) + us_per_mb_part * mb * 2.0 * grid * kHeads * kDv * 4.0;
+      t += t_sep0 + t_sep_split * nsplit + us_per_mb_part * mb * 2.0 * B * nsplit * kHeads * kDv * 4.0;
   }
   return t;
 }
@@ -119,11 +120,11 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
   int rc = check_shape(shape);
   if (rc) return rc;
   if (!out || !workspace_bytes || num_cus < 1) return SMLA_ERR_INVALID_ARG;
-  smla_plan p = {0, kTile, kHeads, 1, SMLA_MERGE_AUTO};
+  smla_plan p = {0, kTile, kHpw, 1, SMLA_MERGE_AUTO};
   if (ov) {
     if (ov->nsplit < 0 || ov->nsplit > kTiles) return SMLA_ERR_PLAN;
     if (ov->tile_tokens != 0 && ov->tile_tokens != kTile) return SMLA_ERR_PLAN;
-    if (ov->heads_per_wg != 0 && ov->heads_per_wg != kHeads) return SMLA_ERR_PLAN;
+    if (ov->heads_per_wg != 0 && ov->heads_per_wg != kHpw) return SMLA_ERR_PLAN;
     if (ov->wg_per_cu < 0 || ov->wg_per_cu > 1) return SMLA_ERR_PLAN;
     if (ov->merge < SMLA_MERGE_AUTO || ov->merge > SMLA_MERGE_SEPARATE) return SMLA_ERR_PLAN;
     p.nsplit = ov->nsplit;
@@ -235,12 +236,12 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
   if (rc || pr.B == 0) return rc;
   if (pr.nsplit > 1 && pr.merge == SMLA_MERGE_SEPARATE) {
     pr.split.counters = nullptr;       // partials only; the combine launch merges them
-    if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_split(pr.split, pr.fmt, pr.B * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_combine(pr.combine, pr.B, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
     return SMLA_OK;
   }
   // one launch: the last split of each request merges the partials
-  if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  if (launch_split(pr.split, pr.fmt, pr.B * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 
@@ -253,7 +254,7 @@ int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_ta
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
   pr.split.counters = nullptr;          // partials only; smla_decode_combine merges them
-  if (launch_split(pr.split, pr.fmt, pr.B * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  if (launch_split(pr.split, pr.fmt, pr.B * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 

@@ -7,6 +7,8 @@
 namespace smla {
 
 constexpr int kHeads = 64;
+constexpr int kHpw = 32;        // query heads per split-kernel workgroup
+constexpr int kHeadGroups = kHeads / kHpw;
 constexpr int kDqk = 576;
 constexpr int kDl = 512;        // latent dims
 constexpr int kDv = 512;
@@ -38,7 +40,7 @@ struct SplitArgs {
   float* part_lse;             // [B][nsplit][64] natural-log lse of each split
   uint16_t* out;               // bf16 [B][64][512] (written directly when nsplit == 1)
   float* lse;                  // [B][64]
-  uint32_t* counters;          // [B][2] tickets / finished writes; non-null: the last split merges
+  uint32_t* counters;          // [B][head group][2] tickets / finished writes; non-null: the last split merges
 };
 
 struct CombineArgs {

@@ -32,7 +32,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytesBf16];
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int kPRow = 36;        // floats per P^T row in LDS (32 tokens + 4 pad)
+constexpr int kPRow = 20;        // floats per P^T row in LDS (16 tokens + 4 pad)
 
 template <int FMT> struct RowFmt;
 template <> struct RowFmt<kFmtFp8> {
@@ -112,25 +112,23 @@ template <int FMT> struct TileLayout {
 // wave v (0..3) takes load instructions v, v+4, ... of the tile; the count
 // per wave is DmaCount<FMT>::of(v).
 template <int FMT>
-__device__ __forceinline__ void issue_tile(const uint64_t LDS_AS* rowaddr_s, int tok0,
-                                           uint8_t LDS_AS* lds, int v, int lane) {
+__device__ __forceinline__ void issue_tile(const uint64_t LDS_AS* rowaddr_s, int tok0, uint8_t LDS_AS* lds, int v,
+                                           int lane) {
   using TL = TileLayout<FMT>;
-  constexpr int kChunks = TL::kSlots;
-  constexpr int kInstr = (kChunks + 63) / 64;
+  constexpr int kInstr = (TL::kSlots + 63) / 64;
   constexpr int kPerWave = (kInstr + 3) / 4;
   // all source addresses first (one LDS round trip), then the loads
   const void* src[kPerWave];
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
     const int c = (v + 4 * q) * 64 + lane;
-    const int cc = c < kChunks ? c : 0;
+    const int cc = c < TL::kSlots ? c : 0;
     src[q] = (const void*)(uintptr_t)((rowaddr_s[tok0 + TL::row_of(cc)] & ~1ull) + 16 * TL::chunk_of(cc));
   }
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
     const int j = v + 4 * q;
-    if (j < kInstr && j * 64 + lane < kChunks)
-      dma16(src[q], (uint32_t)(uintptr_t)(lds + j * 64 * 16));
+    if (j < kInstr && j * 64 + lane < TL::kSlots) dma16(src[q], (uint32_t)(uintptr_t)(lds + j * 64 * 16));
   }
 }
 
@@ -287,101 +285,87 @@ __device__ __forceinline__ f32x4 load_run(const float* part_o, int64_t block, ui
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
 }
 
-// The fused merge of request b by its last split `own` (512 threads).  Its
-// own partial is in LDS (`own_part`, workspace-block layout) with its lse in
-// own_lse[h]; the other nsplit - 1 partials and lses are in the workspace.
-// Same weights and the same split-ordered accumulation as the combine kernel;
-// the lse loads and the first partial loads go out together, and each round
-// loads two partials other than the own one: one memory round trip when
-// nsplit <= 3.
+// The fused merge of (request b, head group hb) by its last split `own`
+// (512 threads).  Its own partial is in LDS (`own_part`, at the offsets it has
+// in a workspace block) with its lse in own_lse[h]; the other nsplit - 1
+// partials and lses are in the workspace.  Same weights and the same
+// split-ordered accumulation as the combine kernel; the lse loads and the
+// first partial loads go out together, and each round loads four partials
+// other than the own one: one memory round trip when nsplit <= 5.
 __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, const float* __restrict__ part_lse,
-                                            int nsplit, int b, int own, const uint8_t* own_part, const float* own_lse,
-                                            uint16_t* __restrict__ out, float* __restrict__ lse, float* wt) {
+                                            int nsplit, int b, int hb, int own, const uint8_t* own_part,
+                                            const float* own_lse, uint16_t* __restrict__ out, float* __restrict__ lse,
+                                            float* wt) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
   const int vb = wave >> 1, db0 = 2 * (wave & 1);
   const int nother = nsplit - 1;
   auto other = [&](int k) { return k < own ? k : k + 1; };    // k-th split other than own, ascending
-  const float* ls = part_lse + (int64_t)b * nsplit * kHeads;
+  const float* ls = part_lse + (int64_t)b * nsplit * kHeads + kHpw * hb;
 
-  // lse of every split (at most two per thread), issued first
-  float lv[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = t + u * kThreads, sp = i >> 6, h = i & (kHeads - 1);
-    lv[u] = i < nsplit * kHeads ? (sp == own ? own_lse[h] : load_agent(ls + sp * kHeads + h)) : 0.f;
-  }
-  f32x4 v[2][2][4][2];
+  // lse of every split for the group's 32 heads (one per thread), issued first
+  const int sp_l = t >> 5, h_l = t & (kHpw - 1);
+  const float lv = sp_l < nsplit ? (sp_l == own ? own_lse[h_l] : load_agent(ls + sp_l * kHeads + h_l)) : 0.f;
+  f32x4 v[4][2][4];
   auto issue = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            v[u][i][j][hb] = k0 + u < nother
-                                 ? load_run(part_o, (int64_t)b * nsplit + other(k0 + u),
-                                            part_run_offset(vb, db0 + i, j, hb, lane))
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+          v[u][i][j] = k0 + u < nother ? load_run(part_o, (int64_t)b * nsplit + other(k0 + u),
+                                                  part_run_offset(vb, db0 + i, j, hb, lane))
+                                       : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   issue(0);
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-    if (t + u * kThreads < nsplit * kHeads) wt[t + u * kThreads] = lv[u];
+  if (sp_l < nsplit) wt[t] = lv;
   lds_barrier();
-  if (t < kHeads)
-    lse[(int64_t)b * kHeads + t] = split_weights(nsplit, [&](int sp) { return wt[sp * kHeads + t]; }, wt + t);
+  if (t < kHpw)   // in place, column t
+    lse[(int64_t)b * kHeads + kHpw * hb + t] =
+        split_weights(nsplit, [&](int sp) { return wt[sp * kHpw + t]; }, wt + t, kHpw);
   lds_barrier();
 
-  f32x4 acc[2][4][2];
+  f32x4 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) acc[i][j][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto add = [&](int sp, auto&& val) {
-    const float w0 = wt[sp * kHeads + l32], w1 = wt[sp * kHeads + 32 + l32];
+    const float w = wt[sp * kHpw + l32];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j][0] += w0 * val(i, j, 0);
-        acc[i][j][1] += w1 * val(i, j, 1);
-      }
+      for (int j = 0; j < 4; ++j) acc[i][j] += w * val(i, j);
   };
-  auto own_val = [&](int i, int j, int hb) {
+  auto own_val = [&](int i, int j) {
     return *reinterpret_cast<const f32x4*>(own_part + part_run_offset(vb, db0 + i, j, hb, lane));
   };
   bool own_done = false;
-  for (int k0 = 0; k0 < nother; k0 += 2) {
+  for (int k0 = 0; k0 < nother; k0 += 4) {
     if (k0 > 0) issue(k0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 4; ++u) {
       if (k0 + u >= nother) break;
       const int sp = other(k0 + u);
       if (!own_done && own < sp) {
         add(own, own_val);
         own_done = true;
       }
-      add(sp, [&](int i, int j, int hb) { return v[u][i][j][hb]; });
+      add(sp, [&](int i, int j) { return v[u][i][j]; });
     }
   }
   if (!own_done) add(own, own_val);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const f32x4 x = acc[i][j][hb];
-        const uint32_t lo = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
-        uint16_t* orow = out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 32 * (db0 + i) + 8 * j + 4 * kg;
-        *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = acc[i][j];
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+      uint16_t* orow = out + ((int64_t)b * kHeads + kHpw * hb + l32) * kDv + 128 * vb + 32 * (db0 + i) + 8 * j + 4 * kg;
+      *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -420,19 +404,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // One LDS block: the tile ring, then P^T.  A merging workgroup reuses its
   // first 128 KB for its own partial output.
   constexpr int kRingBytes = kNbuf * kTileBytes;
-  constexpr int kPBytes = 2 * kHeads * kPRow * 4;
+  constexpr int kPBytes = 2 * 2 * kHpw * kPRow * 4;
   constexpr int kSmem = kRingBytes + kPBytes > (int)kPartBytes ? kRingBytes + kPBytes : (int)kPartBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   uint8_t* const tiles = smem;
   __shared__ uint64_t rowaddr_s[kTopk];            // row address | 1 when masked
   __shared__ uint32_t mask_s[kTiles];              // bit t: token t of the tile is valid
-  // P^T (fp32, unscaled) in [head][token] rows padded to 36 floats so the
-  // 16-byte accesses of 8 consecutive lanes hit distinct banks
-  float (*const p_s)[kHeads][kPRow] = reinterpret_cast<float (*)[kHeads][kPRow]>(smem + kRingBytes);
-  __shared__ float alpha_s[2][kHeads];
-  __shared__ float fin_s[kHeads];
+  // P^T (fp32, unscaled): [buffer][16-token half][head][token], rows padded to
+  // kPRow floats so 16-byte accesses of 16 consecutive lanes hit distinct banks
+  float (*const p_s)[2][kHpw][kPRow] = reinterpret_cast<float (*)[2][kHpw][kPRow]>(smem + kRingBytes);
+  __shared__ float alpha_s[2][2][kHpw];            // [buffer][half][head]
+  __shared__ float mh_s[2][kHpw], lh_s[2][kHpw];   // per half: running max (log2) and sum
   __shared__ int last_s;
-  __shared__ float lsev_s[kHeads];                 // this split's lse per head
+  __shared__ float lsev_s[kHpw];                   // this split's lse per head
   __shared__ int fail_s;
 
   const int lane = threadIdx.x & 63;
@@ -441,18 +425,27 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int c16 = lane & 15;        // column within a 16-wide MFMA tile
   const bool qk_role = wave < 4;
 
+  // work item -> (request, split, head group); the two head groups of one
+  // (request, split) are neighbours, so they run on one XCD and the second
+  // gathers its rows from that XCD's L2
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = w / a.nsplit;
-  const int s = w - b * a.nsplit;
+  const int hg = w & 1;
+  const int bs = w >> 1;
+  const int b = bs / a.nsplit;
+  const int s = bs - b * a.nsplit;
   const int tile0 = s * a.chunk_tiles;
   if (tile0 >= kTiles) return;   // empty split (the host never launches one)
   const int ntiles = min(a.chunk_tiles, kTiles - tile0);
   const int ntok = ntiles * kTile;
   const int ctx = a.ctx_len[b];
   const bool fused = a.nsplit > 1 && a.counters != nullptr;   // merge in this launch
+  uint32_t* const ctr = fused ? a.counters + 2 * (2 * b + hg) : nullptr;   // tickets, finished writes
 
-  // ---- 1. QK waves: raw Q of their 16 heads (lane column = head)
-  const int head = (wave & 3) * 16 + c16;
+  // ---- 1. QK waves: wave q scores heads 16(q&1) .. +15 of the group against
+  // token half q>>1 of every tile; raw Q of those heads (lane column = head)
+  const int hq = wave & 1, mh = (wave >> 1) & 1;
+  const int hloc = 16 * hq + c16;                          // head within the group
+  const int head = kHpw * hg + hloc;                       // head of the request
   const uint16_t* qrow = a.q + ((int64_t)b * kHeads + head) * kDqk;
   bf16x8 qraw[18];
   if (qk_role) {
@@ -490,9 +483,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       mask_s[2 * wave + 1] = (uint32_t)(bits >> 32);
     }
   }
-  // Q must have landed before the first tile load is issued: the tile loads
-  // are invisible to the compiler's wait counting, so any wait it placed for
-  // Q later on would also drain every prefetched tile.
+  // Q must have landed before the barrier: the join of the two roles' code
+  // paths would otherwise leave the compiler a pending Q load to wait for in
+  // the PV waves too, draining their prefetched tiles.
   if (qk_role) {
 #pragma unroll
     for (int c = 0; c < 18; ++c) asm volatile("" : "+v"(qraw[c]));
@@ -500,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   lds_barrier();
 
   // ---- 3. the PV waves issue every tile load (the QK waves never wait on
-  // the texture path); first the prefetch of the first kNbuf tiles
+  // the texture path)
   const int vwave = wave & 3;
   // In iteration k the QK waves start tile k+1 and finish tile k, and the PV
   // waves accumulate tile k-1; tile k + kAhead is issued at the top of
@@ -520,8 +513,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile,
                       (uint8_t LDS_AS*)(tiles + tt * kTileBytes), vwave, lane);
 
-  // Top of iteration k: the PV waves wait for their share of tile k, then a
-  // barrier publishes it; then they issue tile k + kAhead.
+  // Top of iteration k: the PV waves wait for their share of the tile the QK
+  // waves start now, then a barrier publishes it; then they issue more tiles.
   auto iteration_head = [&](int k) {
     const int need = kPipe ? k + 1 : k;   // the tile the QK waves start in iteration k
     const int issued = k == 0 ? npre : min(ntiles, k + kAhead);   // tiles issued so far
@@ -593,8 +586,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       for (int c = 0; c < 18; ++c) qb[c] = qraw[c];
     }
     const float sc_log2 = a.scale_log2 * qscale;
-    float m_run = -INFINITY;        // running max (log2 domain) of this lane's head
+    float m_run = -INFINITY;        // running max (log2 domain) of this head over this token half
     float l_run = 0.f;              // this lane's share of the running sum
+    const int row = 16 * mh + c16;  // tile row this lane's K operand comes from
 
     // Scores are software-pipelined: in iteration k the MFMAs of tile k+1
     // are issued before the softmax of tile k (whose MFMA results came from
@@ -602,91 +596,67 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // cross-lane work.  Raw holds one tile's accumulators before the fp8
     // block scales, which are applied when the tile is finished.
     struct Raw {
-      f32x4 acc[2][FMT == kFmtFp8 ? 4 : 1];   // [16-token half][scale block] (fp8 rows only)
-      f32x4 sm[2];       // rope part (fp8 rows) or the whole score (bf16 rows)
+      f32x4 acc[FMT == kFmtFp8 ? 4 : 1];   // [scale block] (fp8 rows only)
+      f32x4 sm;                             // rope part (fp8 rows) or the whole score (bf16 rows)
     };
     auto issue_scores = [&](int kt, Raw& r) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+      f32x4 sm = {0.f, 0.f, 0.f, 0.f};
       if constexpr (FMT == kFmtBf16) {
-        // one 16-token half at a time (18 operand registers of 4 each)
+        // k-slot group g of 32-dim step c: dims 32c + 8g .. +7 = chunk 4c + g
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int row = 16 * m + c16;
-          f32x4 sm = {0.f, 0.f, 0.f, 0.f};
-          // k-slot group g of 32-dim step c: dims 32c + 8g .. +7 = chunk 4c + g
-#pragma unroll
-          for (int c = 0; c < 18; ++c)
-            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(tb + TL::off(row, 4 * c + g)),
-                                                        qb[c], sm, 0, 0, 0);
-          r.sm[m] = sm;
-        }
+        for (int c = 0; c < 18; ++c)
+          sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(tb + TL::off(row, 4 * c + g)),
+                                                      qb[c], sm, 0, 0, 0);
       } else {
-        i32x8 ka[2][4];
-        bf16x8 kr[2][2];
+        i32x8 ka[4];
+        bf16x8 kr[2];
+        // codes 128blk + 32g .. +31 = chunks 8blk + 2g, +1
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int row = 16 * m + c16;
-          // codes 128blk + 32g .. +31 = chunks 8blk + 2g, +1
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk) {
-            const i32x4 k0 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g));
-            const i32x4 k1 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g + 1));
-            ka[m][blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-          }
-          // rope dims 32c + 8g .. +7 sit at byte 528 + 2 (32c + 8g): chunk 33 + 4c + g
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            kr[m][c] = *reinterpret_cast<const bf16x8*>(tb + TL::off(row, 33 + 4 * c + g));
+        for (int blk = 0; blk < 4; ++blk) {
+          const i32x4 k0 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g));
+          const i32x4 k1 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g + 1));
+          ka[blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
         }
-        // independent MFMA chains per half: hi of every block, rope, then lo
+        // rope dims 32c + 8g .. +7 sit at byte 528 + 2 (32c + 8g): chunk 33 + 4c + g
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < 2; ++c) kr[c] = *reinterpret_cast<const bf16x8*>(tb + TL::off(row, 33 + 4 * c + g));
+        // independent MFMA chains: hi of every block, rope, then lo
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-            r.acc[m][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qhi[blk],
-                                                                            f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        for (int blk = 0; blk < 4; ++blk)
+          r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[blk], qhi[blk], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                       0, 0, 0, 0, 0, 0);
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-            sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[m][c], qb[16 + c], sm, 0, 0, 0);
+        for (int c = 0; c < 2; ++c) sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[c], qb[16 + c], sm, 0, 0, 0);
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
-            r.acc[m][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[m][blk], qlo[blk], r.acc[m][blk], 0, 0,
-                                                                            0, 0, 0, 0);
-          r.sm[m] = sm;
-        }
+        for (int blk = 0; blk < 4; ++blk)
+          r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[blk], qlo[blk], r.acc[blk], 0, 0, 0, 0, 0, 0);
       }
+      r.sm = sm;
     };
     // softmax of tile kt from its raw scores; P^T and alpha to LDS
     auto finish_tile = [&](int kt, bool dry, const Raw& r) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const uint32_t vmask = dry ? 0u : mask_s[kt];
-      f32x4 sacc[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        f32x4 sm = r.sm[m];
-        if constexpr (FMT == kFmtFp8) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 sv = *reinterpret_cast<const float4*>(tb + TL::off(16 * m + 4 * g + i, kDl / 16));
-            sm[i] += r.acc[m][0][i] * sv.x + r.acc[m][1][i] * sv.y + r.acc[m][2][i] * sv.z + r.acc[m][3][i] * sv.w;
-          }
-        }
-        sacc[m] = sm;
-      }
-
-      // online softmax (log2 domain); masked slots score -inf
-      float p[8];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
+      f32x4 sacc = r.sm;
+      if constexpr (FMT == kFmtFp8) {
+        // this lane's tokens are 16mh + 4g + i of the tile
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = (vmask >> (16 * m + 4 * g + i)) & 1u;
-          const float v = ok ? sacc[m][i] * sc_log2 : -INFINITY;
-          p[4 * m + i] = v;
-          tmax = fmaxf(tmax, v);
+          const float4 sv = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
+          sacc[i] += r.acc[0][i] * sv.x + r.acc[1][i] * sv.y + r.acc[2][i] * sv.z + r.acc[3][i] * sv.w;
         }
+      }
+      // online softmax (log2 domain) over this half; masked slots score -inf
+      float p[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (vmask >> (16 * mh + 4 * g + i)) & 1u;
+        const float v = ok ? sacc[i] * sc_log2 : -INFINITY;
+        p[i] = v;
+        tmax = fmaxf(tmax, v);
+      }
       tmax = wave_max16(tmax);
       float m_cur = dry ? -INFINITY : m_run;
       float alpha = 1.0f;
@@ -698,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       const float m_use = (m_cur == -INFINITY) ? 0.f : m_cur;
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         p[i] = __builtin_amdgcn_exp2f(p[i] - m_use);
         psum += p[i];
       }
@@ -706,15 +676,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         m_run = m_cur;
         l_run = l_run * alpha + psum;
       }
-
-      // P^T rows (fp32, unscaled) for the PV waves; this lane holds tokens
-      // 16m + 4g .. +3 of its head
+      // P^T row of this head and half: tokens 4g .. 4g+3
       const int pb = kt & 1;
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        *reinterpret_cast<float4*>(&p_s[pb][head][16 * m + 4 * g]) =
-            make_float4(p[4 * m], p[4 * m + 1], p[4 * m + 2], p[4 * m + 3]);
-      if (g == 0) alpha_s[pb][head] = alpha;
+      *reinterpret_cast<float4*>(&p_s[pb][mh][hloc][4 * g]) = make_float4(p[0], p[1], p[2], p[3]);
+      if (g == 0) alpha_s[pb][mh][hloc] = alpha;
     };
     // One iteration: k = -1 is a warm-up pass through the same code on
     // whatever buffer 0 holds, every slot masked and its state thrown away,
@@ -756,30 +721,28 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     }
 
     // This split's scores are done (only the PV waves' last tile is left,
-    // which waits on nothing): take the request's arrival ticket now, so its
-    // latency overlaps that tile.  The holder of the last ticket merges.
+    // which waits on nothing): take the arrival ticket of this (request, head
+    // group) now, so its latency overlaps that tile.  The holder of the last
+    // ticket merges.
     if (fused && threadIdx.x == 0)
-      last_s = __hip_atomic_fetch_add(&a.counters[2 * b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      last_s = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                (uint32_t)(a.nsplit - 1);
-    // normaliser of each head for the PV waves; lse from here
+    // this half's max and sum of each head for the PV waves
     const float L = wave_sum16(l_run);
-    const float lse_v = L > 0.f ? (m_run + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
     if (g == 0) {
-      fin_s[head] = L;
-      lsev_s[head] = lse_v;
-      if (a.nsplit == 1) a.lse[(int64_t)b * kHeads + head] = lse_v;
+      mh_s[mh][hloc] = m_run;
+      lh_s[mh][hloc] = L;
     }
     lds_barrier();
-    if (a.nsplit > 1 && !(fused && last_s) && g == 0)
-      store_agent(a.part_lse + ((int64_t)b * a.nsplit + s) * kHeads + head, lse_v);
   } else {
     // ---------------------------------------------------------------- PV role
-    // 32x32x16 bf16 MFMA: O^T[32 d][32 heads] += V^T[32 d][16 tok] . P^T[16 tok][32 heads].
+    // 32x32x16 bf16 MFMA: O^T[32 d][32 heads] += V^T[32 d][16 tok] . P^T[16 tok][32 heads],
+    // one accumulator per 16-token half (each half has its own running max).
     // Operand lane layout (both): row/col = lane % 32, k = 8 * (lane / 32) + i,
-    // so k-slot (lane/32, i) of k-half kh is token 16kh + 8(lane/32) + i.
+    // so k-slot (lane/32, i) of half kh is token 16kh + 8(lane/32) + i.
     const int vb = wave - 4;          // scale block / 128-dim slice of the latent
     const int l32 = lane & 31, kg = lane >> 5;
-    f32x16 o[4][2];                   // [32-dim block of the slice][32-head block]
+    f32x16 o[4][2];                   // [32-dim block of the slice][token half]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -795,9 +758,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       const int kt = dry ? 0 : k - 1;   // tile accumulated in this iteration
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const int pb = dry ? 1 : kt & 1;
-      // P^T operands [head block][k-half]: 8 tokens 16kh + 8kg + i of head
-      // 32hb + l32, times this slice's block scale for fp8 rows, in bf16
-      bf16x8 pv[2][2];
+      // P^T operands per half: 8 tokens 16kh + 8kg + i of head l32, times this
+      // slice's block scale for fp8 rows, in bf16
+      bf16x8 pv[2];
       float al[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
@@ -806,25 +769,21 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         for (int i = 0; i < 8; ++i)
           sc[i] = (FMT == kFmtFp8) ? *reinterpret_cast<const float*>(tb + TL::off(16 * kh + 8 * kg + i, kDl / 16) + 4 * vb)
                                    : 1.0f;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const float4 p0 = *reinterpret_cast<const float4*>(&p_s[pb][32 * hb + l32][16 * kh + 8 * kg]);
-          const float4 p1 = *reinterpret_cast<const float4*>(&p_s[pb][32 * hb + l32][16 * kh + 8 * kg + 4]);
-          bf16x8 v;
-          v[0] = (__bf16)(p0.x * sc[0]); v[1] = (__bf16)(p0.y * sc[1]);
-          v[2] = (__bf16)(p0.z * sc[2]); v[3] = (__bf16)(p0.w * sc[3]);
-          v[4] = (__bf16)(p1.x * sc[4]); v[5] = (__bf16)(p1.y * sc[5]);
-          v[6] = (__bf16)(p1.z * sc[6]); v[7] = (__bf16)(p1.w * sc[7]);
-          pv[hb][kh] = v;
-        }
+        const float4 p0 = *reinterpret_cast<const float4*>(&p_s[pb][kh][l32][8 * kg]);
+        const float4 p1 = *reinterpret_cast<const float4*>(&p_s[pb][kh][l32][8 * kg + 4]);
+        bf16x8 v;
+        v[0] = (__bf16)(p0.x * sc[0]); v[1] = (__bf16)(p0.y * sc[1]);
+        v[2] = (__bf16)(p0.z * sc[2]); v[3] = (__bf16)(p0.w * sc[3]);
+        v[4] = (__bf16)(p1.x * sc[4]); v[5] = (__bf16)(p1.y * sc[5]);
+        v[6] = (__bf16)(p1.z * sc[6]); v[7] = (__bf16)(p1.w * sc[7]);
+        pv[kh] = v;
+        al[kh] = alpha_s[pb][kh][l32];
       }
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) al[hb] = alpha_s[pb][32 * hb + l32];
+      for (int kh = 0; kh < 2; ++kh)
+        if (__builtin_amdgcn_ballot_w64(al[kh] != 1.0f)) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        if (__builtin_amdgcn_ballot_w64(al[hb] != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < 4; ++db) o[db][hb] *= al[hb];
+          for (int db = 0; db < 4; ++db) o[db][kh] *= al[kh];
         }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
@@ -854,9 +813,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
             const i32x4 packed = {a0[0], a0[1], a1[0], a1[1]};
             va = __builtin_bit_cast(bf16x8, packed);
           }
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-            o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[hb][kh], o[db][hb], 0, 0, 0);
+          o[db][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[kh], o[db][kh], 0, 0, 0);
         }
       if (dry) {
 #pragma unroll
@@ -866,56 +823,63 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       }
     }
 
-    lds_barrier();                    // QK waves have published the normalisers
-    float inv[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const float Lh = fin_s[32 * hb + l32];
-      inv[hb] = Lh > 0.f ? 1.0f / Lh : 0.f;
+    lds_barrier();                    // QK waves have published each half's max and sum
+    // combine the two halves of head l32:
+    //   M = max(m0, m1), L = l0 2^(m0-M) + l1 2^(m1-M), out = (O0 2^(m0-M) + O1 2^(m1-M)) / L
+    float f[2];
+    float lse_v;
+    {
+      const float m0 = mh_s[0][l32], m1 = mh_s[1][l32];
+      const float M = fmaxf(m0, m1);
+      const float e0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+      const float e1 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      const float Lh = lh_s[0][l32] * e0 + lh_s[1][l32] * e1;
+      const float inv = Lh > 0.f ? 1.0f / Lh : 0.f;
+      f[0] = e0 * inv;
+      f[1] = e1 * inv;
+      lse_v = Lh > 0.f ? (M + __builtin_amdgcn_logf(Lh)) * kLn2 : -INFINITY;
     }
-    // register j of o[db][hb] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head = 32hb + l32]
+    const int ghead = kHpw * hg + l32;
+    if (vb == 0 && kg == 0) {
+      lsev_s[l32] = lse_v;
+      if (a.nsplit == 1) a.lse[(int64_t)b * kHeads + ghead] = lse_v;
+      else if (!(fused && last_s)) store_agent(a.part_lse + ((int64_t)b * a.nsplit + s) * kHeads + ghead, lse_v);
+    }
+    // register j of o[db][*] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head l32]
+    f32x16 res[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) res[db] = o[db][0] * f[0] + o[db][1] * f[1];
     if (a.nsplit == 1) {
+      uint16_t* orow = a.out + ((int64_t)b * kHeads + ghead) * kDv + 128 * vb + 4 * kg;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        uint16_t* orow = a.out + ((int64_t)b * kHeads + 32 * hb + l32) * kDv + 128 * vb + 4 * kg;
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float v0 = o[db][hb][4 * jj], v1 = o[db][hb][4 * jj + 1];
-            const float v2 = o[db][hb][4 * jj + 2], v3 = o[db][hb][4 * jj + 3];
-            const uint32_t lo = (uint32_t)f32_to_bf16_rne(v0 * inv[hb]) | ((uint32_t)f32_to_bf16_rne(v1 * inv[hb]) << 16);
-            const uint32_t hi = (uint32_t)f32_to_bf16_rne(v2 * inv[hb]) | ((uint32_t)f32_to_bf16_rne(v3 * inv[hb]) << 16);
-            *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
-          }
-      }
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[db][4 * jj]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[db][4 * jj + 2]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 3]) << 16);
+          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
+        }
     } else if (!fused || !last_s) {
       const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)b * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const f32x4 v = {o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb],
-                             o[db][hb][4 * jj + 2] * inv[hb], o[db][hb][4 * jj + 3] * inv[hb]};
-            if (fused)   // read back in this launch, possibly on another XCD
-              __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, kSc1);
-            else         // read by the combine launch
-              __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hb, lane), 0, 0);
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 v = {res[db][4 * jj], res[db][4 * jj + 1], res[db][4 * jj + 2], res[db][4 * jj + 3]};
+          if (fused)   // read back in this launch, possibly on another XCD
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hg, lane), 0, kSc1);
+          else         // read by the combine launch
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hg, lane), 0, 0);
+        }
     } else {
-      // last split of the request: its own partial goes to LDS, in the
-      // layout of a workspace block
+      // last split of this (request, head group): its own partial goes to
+      // LDS, at the offsets it has in a workspace block
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, db, jj, hb, lane)) =
-                f32x4{o[db][hb][4 * jj] * inv[hb], o[db][hb][4 * jj + 1] * inv[hb], o[db][hb][4 * jj + 2] * inv[hb],
-                      o[db][hb][4 * jj + 3] * inv[hb]};
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, db, jj, hg, lane)) =
+              f32x4{res[db][4 * jj], res[db][4 * jj + 1], res[db][4 * jj + 2], res[db][4 * jj + 3]};
     }
   }
 
@@ -924,8 +888,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   if (!last_s) {
     wait_stores();                       // this wave's partial stores have completed ...
     lds_barrier();                       // ... and so have every other wave's
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(&a.counters[2 * b + 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(&ctr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   // Last ticket: wait until the splits with earlier tickets (all resident and
@@ -934,17 +897,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   if (threadIdx.x == 0) {
     bool ok = false;
     for (int it = 0; it < kSpinLimit && !ok; ++it) {
-      ok = __hip_atomic_load(&a.counters[2 * b + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-           (uint32_t)(a.nsplit - 1);
+      ok = __hip_atomic_load(&ctr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(a.nsplit - 1);
       if (!ok) __builtin_amdgcn_s_sleep(2);
     }
     fail_s = ok ? 0 : 1;
-    a.counters[2 * b] = 0u;              // both counters back to zero for the next call
-    a.counters[2 * b + 1] = 0u;
+    ctr[0] = 0u;                         // both counters back to zero for the next call
+    ctr[1] = 0u;
   }
   lds_barrier();
-  merge_fused(a.part_o, a.part_lse, a.nsplit, b, s, smem, lsev_s, a.out, a.lse, reinterpret_cast<float*>(rowaddr_s));
-  if (fail_s && threadIdx.x < kHeads) a.lse[(int64_t)b * kHeads + threadIdx.x] = __builtin_nanf("");
+  merge_fused(a.part_o, a.part_lse, a.nsplit, b, hg, s, smem, lsev_s, a.out, a.lse,
+              reinterpret_cast<float*>(rowaddr_s));
+  if (fail_s && threadIdx.x < kHpw) a.lse[(int64_t)b * kHeads + kHpw * hg + threadIdx.x] = __builtin_nanf("");
 }
 
 // ----------------------------------------------------------------------------

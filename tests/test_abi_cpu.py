@@ -73,7 +73,7 @@ def test_null_pointers_and_bad_scale():
 
 def test_plan_overrides_validated():
     s = _shape()
-    for bad in ({"nsplit": 17}, {"nsplit": -1}, {"tile_tokens": 16}, {"heads_per_wg": 32}, {"wg_per_cu": 3},
+    for bad in ({"nsplit": 17}, {"nsplit": -1}, {"tile_tokens": 16}, {"heads_per_wg": 64}, {"wg_per_cu": 3},
                 {"merge": 3}, {"merge": -1}):
         with pytest.raises(smla.SmlaError) as e:
             smla.plan_for_cus(s, 256, bad)
@@ -88,8 +88,8 @@ def test_forced_nsplit_normalised_to_whole_tiles(forced, expect):
     chunk = math.ceil(16 / p.nsplit)
     assert (p.nsplit - 1) * chunk < 16 <= p.nsplit * chunk
     a256 = lambda x: (x + 255) // 256 * 256
-    # partial outputs, partial lse, two counters per request (tickets, finished writes)
-    assert ws == (0 if expect == 1 else a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4) + a256(8 * 8))
+    # partial outputs, partial lse, two counters (tickets, finished writes) per request and head group
+    assert ws == (0 if expect == 1 else a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4) + a256(8 * 16))
 
 
 def test_selector_is_shape_only_and_bounded():
