@@ -20,6 +20,7 @@
 namespace smla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -32,7 +33,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytesBf16];
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int kPRow = 20;        // floats per P^T row in LDS (16 tokens + 4 pad)
+constexpr int kPRow = 24;        // bf16 per P^T row in LDS (16 tokens + 8 pad: 48-byte rows, so the
+                                 // 16-byte reads of 16 consecutive lanes hit distinct banks)
 
 template <int FMT> struct RowFmt;
 template <> struct RowFmt<kFmtFp8> {
@@ -404,15 +406,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // One LDS block: the tile ring, then P^T.  A merging workgroup reuses its
   // first 128 KB for its own partial output.
   constexpr int kRingBytes = kNbuf * kTileBytes;
-  constexpr int kPBytes = 2 * 2 * kHpw * kPRow * 4;
+  // P^T copies: one per 128-dim scale block (fp8 rows: P times that block's
+  // scale) or a single one (bf16 rows)
+  constexpr int kPCopies = FMT == kFmtFp8 ? 4 : 1;
+  constexpr int kPBytes = 2 * kPCopies * 2 * kHpw * kPRow * 2;
   constexpr int kSmem = kRingBytes + kPBytes > (int)kPartBytes ? kRingBytes + kPBytes : (int)kPartBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   uint8_t* const tiles = smem;
   __shared__ uint64_t rowaddr_s[kTopk];            // row address | 1 when masked
   __shared__ uint32_t mask_s[kTiles];              // bit t: token t of the tile is valid
-  // P^T (fp32, unscaled): [buffer][16-token half][head][token], rows padded to
-  // kPRow floats so 16-byte accesses of 16 consecutive lanes hit distinct banks
-  float (*const p_s)[2][kHpw][kPRow] = reinterpret_cast<float (*)[2][kHpw][kPRow]>(smem + kRingBytes);
+  // P^T in bf16, already multiplied by the token's scale of the copy's block:
+  // [buffer][copy][16-token half][head][token]
+  __bf16 (*const p_s)[kPCopies][2][kHpw][kPRow] =
+      reinterpret_cast<__bf16 (*)[kPCopies][2][kHpw][kPRow]>(smem + kRingBytes);
   __shared__ float alpha_s[2][2][kHpw];            // [buffer][half][head]
   __shared__ float mh_s[2][kHpw], lh_s[2][kHpw];   // per half: running max (log2) and sum
   __shared__ int last_s;
@@ -639,12 +645,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const uint32_t vmask = dry ? 0u : mask_s[kt];
       f32x4 sacc = r.sm;
+      float4 sv[4];                 // block scales of this lane's tokens 16mh + 4g + i
       if constexpr (FMT == kFmtFp8) {
-        // this lane's tokens are 16mh + 4g + i of the tile
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 sv = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
-          sacc[i] += r.acc[0][i] * sv.x + r.acc[1][i] * sv.y + r.acc[2][i] * sv.z + r.acc[3][i] * sv.w;
+          sv[i] = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
+          sacc[i] += r.acc[0][i] * sv[i].x + r.acc[1][i] * sv[i].y + r.acc[2][i] * sv[i].z + r.acc[3][i] * sv[i].w;
         }
       }
       // online softmax (log2 domain) over this half; masked slots score -inf
@@ -676,9 +682,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         m_run = m_cur;
         l_run = l_run * alpha + psum;
       }
-      // P^T row of this head and half: tokens 4g .. 4g+3
+      // P^T row of this head and half, tokens 4g .. 4g+3, one bf16 copy per
+      // scale block with the block's scale folded in (the PV operand as is)
       const int pb = kt & 1;
-      *reinterpret_cast<float4*>(&p_s[pb][mh][hloc][4 * g]) = make_float4(p[0], p[1], p[2], p[3]);
+#pragma unroll
+      for (int cp = 0; cp < kPCopies; ++cp) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(FMT == kFmtFp8 ? p[i] * (&sv[i].x)[cp] : p[i]);
+        *reinterpret_cast<bf16x4*>(&p_s[pb][cp][mh][hloc][4 * g]) = v;
+      }
       if (g == 0) alpha_s[pb][mh][hloc] = alpha;
     };
     // One iteration: k = -1 is a warm-up pass through the same code on
@@ -758,25 +771,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       const int kt = dry ? 0 : k - 1;   // tile accumulated in this iteration
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const int pb = dry ? 1 : kt & 1;
-      // P^T operands per half: 8 tokens 16kh + 8kg + i of head l32, times this
-      // slice's block scale for fp8 rows, in bf16
+      // P^T operands per half: 8 tokens 16kh + 8kg + i of head l32, from this
+      // slice's copy (the block scale is already in)
+      constexpr int kPCopies = FMT == kFmtFp8 ? 4 : 1;
+      const int cp = kPCopies == 4 ? vb : 0;
       bf16x8 pv[2];
       float al[2];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        float sc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          sc[i] = (FMT == kFmtFp8) ? *reinterpret_cast<const float*>(tb + TL::off(16 * kh + 8 * kg + i, kDl / 16) + 4 * vb)
-                                   : 1.0f;
-        const float4 p0 = *reinterpret_cast<const float4*>(&p_s[pb][kh][l32][8 * kg]);
-        const float4 p1 = *reinterpret_cast<const float4*>(&p_s[pb][kh][l32][8 * kg + 4]);
-        bf16x8 v;
-        v[0] = (__bf16)(p0.x * sc[0]); v[1] = (__bf16)(p0.y * sc[1]);
-        v[2] = (__bf16)(p0.z * sc[2]); v[3] = (__bf16)(p0.w * sc[3]);
-        v[4] = (__bf16)(p1.x * sc[4]); v[5] = (__bf16)(p1.y * sc[5]);
-        v[6] = (__bf16)(p1.z * sc[6]); v[7] = (__bf16)(p1.w * sc[7]);
-        pv[kh] = v;
+        pv[kh] = *reinterpret_cast<const bf16x8*>(&p_s[pb][cp][kh][l32][8 * kg]);
         al[kh] = alpha_s[pb][kh][l32];
       }
 #pragma unroll
