@@ -100,10 +100,10 @@ template <int FMT> struct TileLayout {
     return 16u * (uint32_t)(chunk < 4 * kGroups ? ((chunk >> 2) * 2 + (row >> 4)) * 64 + (chunk & 3) * 16 + (row & 15)
                                                 : kTail + (chunk - 4 * kGroups) * kTile + row);
   }
-  __device__ static constexpr int row_of(int slot) {
+  __host__ __device__ static constexpr int row_of(int slot) {
     return slot < kTail ? 16 * ((slot >> 6) & 1) + (slot & 15) : (slot - kTail) % kTile;
   }
-  __device__ static constexpr int chunk_of(int slot) {
+  __host__ __device__ static constexpr int chunk_of(int slot) {
     return slot < kTail ? 4 * (slot >> 7) + ((slot >> 4) & 3) : 4 * kGroups + (slot - kTail) / kTile;
   }
 };
@@ -113,26 +113,62 @@ template <int FMT> struct TileLayout {
 // row when the slot is masked; bit 0 of the address marks that).  Issuing
 // wave v (0..3) takes load instructions v, v+4, ... of the tile; the count
 // per wave is DmaCount<FMT>::of(v).
+//
+// Instruction j < 2 kGroups fills slots 64j + lane: row 16 (j & 1) + lane % 16,
+// chunk 4 (j >> 1) + lane / 16.  A wave's instructions all have j & 1 = v & 1,
+// so each lane reads one row for all of them, at offsets 64 (j >> 1) past its
+// chunk; the tail instruction (fp8 rows) reads row lane % 32 of the chunks
+// after the groups.  TileSrc holds those two per-lane addresses, so they can
+// be read from LDS a tile ahead of the loads.
+struct TileSrc {
+  uint64_t main, tail;   // row addresses as stored (bit 0: masked row)
+};
 template <int FMT>
-__device__ __forceinline__ void issue_tile(const uint64_t LDS_AS* rowaddr_s, int tok0, uint8_t LDS_AS* lds, int v,
-                                           int lane) {
+__device__ __forceinline__ TileSrc tile_src(const uint64_t LDS_AS* rowaddr_s, int tok0, int v, int lane) {
   using TL = TileLayout<FMT>;
+  constexpr int kFull = 2 * TL::kGroups;
+  constexpr int kInstr = (TL::kSlots + 63) / 64;
+  static_assert(TL::kSlots - TL::kTail <= 64, "at most one tail instruction");
+  TileSrc s;
+  s.main = rowaddr_s[tok0 + 16 * (v & 1) + (lane & 15)];
+  s.tail = 0;
+  if (kInstr > kFull && v == kFull % 4) s.tail = rowaddr_s[tok0 + (lane & 31)];
+  return s;
+}
+// The per-lane addresses above cover the layout exactly (checked over every slot).
+template <int FMT> constexpr bool tile_src_covers_layout() {
+  using TL = TileLayout<FMT>;
+  for (int slot = 0; slot < TL::kSlots; ++slot) {
+    const int j = slot / 64, lane = slot % 64;
+    const bool full = j < 2 * TL::kGroups;
+    const int row = full ? 16 * (j & 1) + lane % 16 : lane % 32;
+    const int chunk = full ? 4 * (j >> 1) + lane / 16 : 4 * TL::kGroups + lane / 32;
+    if (row != TL::row_of(slot) || chunk != TL::chunk_of(slot)) return false;
+  }
+  return true;
+}
+static_assert(tile_src_covers_layout<kFmtFp8>() && tile_src_covers_layout<kFmtBf16>(), "tile source layout");
+template <int FMT>
+__device__ __forceinline__ void issue_tile(const TileSrc& s, uint8_t LDS_AS* lds, int v, int lane) {
+  using TL = TileLayout<FMT>;
+  constexpr int kFull = 2 * TL::kGroups;
   constexpr int kInstr = (TL::kSlots + 63) / 64;
   constexpr int kPerWave = (kInstr + 3) / 4;
-  // all source addresses first (one LDS round trip), then the loads
-  const void* src[kPerWave];
-#pragma unroll
-  for (int q = 0; q < kPerWave; ++q) {
-    const int c = (v + 4 * q) * 64 + lane;
-    const int cc = c < TL::kSlots ? c : 0;
-    src[q] = (const void*)(uintptr_t)((rowaddr_s[tok0 + TL::row_of(cc)] & ~1ull) + 16 * TL::chunk_of(cc));
-  }
+  const uint64_t main = (s.main & ~1ull) + 16 * (lane >> 4);
+  const uint64_t tail = (s.tail & ~1ull) + 16 * (4 * TL::kGroups + (lane >> 5));
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
     const int j = v + 4 * q;
-    if (j < kInstr && j * 64 + lane < TL::kSlots) dma16(src[q], (uint32_t)(uintptr_t)(lds + j * 64 * 16));
+    if (j < kFull)
+      dma16((const void*)(uintptr_t)(main + 64 * (j >> 1)), (uint32_t)(uintptr_t)(lds + j * 64 * 16));
+    else if (j < kInstr && lane < TL::kSlots - TL::kTail)
+      dma16((const void*)(uintptr_t)tail, (uint32_t)(uintptr_t)(lds + j * 64 * 16));
   }
 }
+
+// Raw V^T operand of one PV MFMA as read from LDS: 8 fp8 codes or 8 bf16.
+template <int FMT> struct VRaw { typedef i32x2 type; };
+template <> struct VRaw<kFmtBf16> { typedef i32x4 type; };
 
 template <int FMT> struct DmaCount {
   static constexpr int kChunks = kTile * (RowFmt<FMT>::kRow / 16);
@@ -207,6 +243,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// Workgroup barrier that orders nothing of this wave's own memory accesses
+// (only the compiler's view of them): for a wave that has written no LDS
+// since the last barrier, whose LDS reads may then stay in flight across it.
+__device__ __forceinline__ void arrive_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Partial results travel between workgroups of one launch that may sit on
 // different XCDs, whose L2 caches are not kept coherent with each other.
@@ -514,30 +555,25 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // workgroup starts at once, and a deeper first burst would delay everyone's
   // first tile behind the others' later ones.  The rest follow at its top.
   const int npre = min(kPipe ? 2 : kAhead, ntiles);
+  auto src_of = [&](int tt) { return tile_src<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile, vwave, lane); };
+  auto issue = [&](int tt, const TileSrc& src) {
+    issue_tile<FMT>(src, (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), vwave, lane);
+  };
   if (!qk_role)
-    for (int tt = 0; tt < npre; ++tt)
-      issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile,
-                      (uint8_t LDS_AS*)(tiles + tt * kTileBytes), vwave, lane);
+    for (int tt = 0; tt < npre; ++tt) issue(tt, src_of(tt));
 
   // Top of iteration k: the PV waves wait for their share of the tile the QK
   // waves start now, then a barrier publishes it; then they issue more tiles.
-  auto iteration_head = [&](int k) {
+  auto wait_tile_loads = [&](int k) {
     const int need = kPipe ? k + 1 : k;   // the tile the QK waves start in iteration k
     const int issued = k == 0 ? npre : min(ntiles, k + kAhead);   // tiles issued so far
-    if (!qk_role && need < ntiles) {
+    if (need < ntiles) {
       const int after = issued - need - 1;                    // tiles issued after it
       if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(after);
       else wait_tiles<DmaCount<FMT>::of(3)>(after);
-    } else if (!qk_role && k < ntiles) {
+    } else if (k < ntiles) {
       if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(0);
       else wait_tiles<DmaCount<FMT>::of(3)>(0);
-    }
-    lds_barrier();
-    if (!qk_role) {
-      // tile k + kAhead (at k = 0 also the ones the prefetch left out)
-      for (int tt = k == 0 ? npre : k + kAhead; tt <= k + kAhead && tt < ntiles; ++tt)
-        issue_tile<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile,
-                        (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), vwave, lane);
     }
   };
 
@@ -704,12 +740,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       const bool dry = k < 0;
       if constexpr (kPipe) {   // (the bf16 ring runs the unpipelined loop below)
         if (k <= 0) {
-          if (!dry) iteration_head(0);
+          if (!dry) lds_barrier();
           issue_scores(0, cur);
         }
         if (k + 1 < ntiles) issue_scores(k + 1, nxt);
         finish_tile(dry ? 0 : k, dry, cur);
-        if (!dry) iteration_head(k + 1);
+        if (!dry) lds_barrier();
       }
     };
     Raw ra, rb;
@@ -725,7 +761,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma clang loop unroll(disable)
       for (int k = kfirst; k <= ntiles; ++k) {
         const bool dry = k < 0;
-        if (!dry) iteration_head(k);
+        if (!dry) lds_barrier();
         if (k == ntiles) break;
         Raw r;
         issue_scores(dry ? 0 : k, r);
@@ -756,20 +792,74 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     const int vb = wave - 4;          // scale block / 128-dim slice of the latent
     const int l32 = lane & 31, kg = lane >> 5;
     f32x16 o[4][2];                   // [32-dim block of the slice][token half]
+    // zero from an asm statement, so the compiler cannot hoist the zeroing
+    // above the role branch and keep 128 registers live through the QK path
+    float zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
+      for (int j = 0; j < 2; ++j) o[i][j] = zero;
 
+    // V^T operands of the tile accumulated next, as read from LDS: they are
+    // read one iteration ahead (tile k at the end of iteration k, after the
+    // MFMAs of tile k-1), so their latency hides under the MFMAs and the
+    // barrier.  Tile k is published by the barrier of iteration k - 1 (k when
+    // unpipelined) and its buffer is reloaded only in iteration k + 2.
+    typename VRaw<FMT>::type vnext[2][4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vnext[kh][db] = {};
+    auto read_v = [&](int kt) {
+      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+      const int gg = lane >> 4;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          if constexpr (FMT == kFmtFp8) {
+            // 16-lane group gg reads tokens 16kh + 8(gg>>1) + 0..7 x dims
+            // 32db + 16(gg&1) + 0..15; source lane (2r + half) supplies 8 bytes of row r
+            const int r = c16 >> 1, half = c16 & 1;
+            const uint8_t* src = tb + TL::off(16 * kh + 8 * (gg >> 1) + r, 8 * vb + 2 * db + (gg & 1)) + 8 * half;
+            vnext[kh][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
+          } else {
+            // two 4-row reads per group: rows 16kh + 8(gg>>1) + 0..3 and + 4..7;
+            // source lane (4r + q) supplies 4 elements of row r
+            const int r = c16 >> 2, q = c16 & 3;
+            // dims 128vb + 32db + 16(gg&1) + 4q .. +3: chunk 16vb + 4db + 2(gg&1) + q/2, byte 8(q&1)
+            const int row = 16 * kh + 8 * (gg >> 1) + r, chunk = 16 * vb + 4 * db + 2 * (gg & 1) + (q >> 1);
+            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(tb + TL::off(row, chunk) + 8 * (q & 1)));
+            const i16x4 r1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(tb + TL::off(row + 4, chunk) + 8 * (q & 1)));
+            // whole-vector bit casts: element-wise short -> __bf16 casts of this
+            // result were mis-lowered (the upper dword was dropped)
+            const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
+            const i32x2 a1 = __builtin_bit_cast(i32x2, r1);
+            vnext[kh][db] = i32x4{a0[0], a0[1], a1[0], a1[1]};
+          }
+        }
+    };
+
+    TileSrc nsrc{0, 0};               // load sources of the next tile to issue
     // Iteration 0 has no P yet: it is a warm-up pass through the same loop
-    // code on tile 0 and an unwritten P buffer (loading the instructions into
-    // the cache while the QK waves score tile 0); its accumulators are reset.
+    // code on zero operands and an unwritten P buffer (loading the
+    // instructions into the cache while the QK waves score tile 0); its
+    // accumulators are reset.
 #pragma clang loop unroll(disable)
     for (int k = 0; k <= ntiles; ++k) {
-      iteration_head(k);
+      wait_tile_loads(k);
+      arrive_barrier();
+      if (k == 0) {
+        for (int tt = npre; tt <= kAhead && tt < ntiles; ++tt) issue(tt, src_of(tt));
+        if (kAhead + 1 < ntiles) nsrc = src_of(kAhead + 1);
+      } else if (k + kAhead < ntiles) {
+        issue(k + kAhead, nsrc);
+        if (k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
+      }
       const bool dry = k == 0;
       const int kt = dry ? 0 : k - 1;   // tile accumulated in this iteration
-      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const int pb = dry ? 1 : kt & 1;
       // P^T operands per half: 8 tokens 16kh + 8kg + i of head l32, from this
       // slice's copy (the block scale is already in)
@@ -794,27 +884,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         for (int db = 0; db < 4; ++db) {
           bf16x8 va;
           if constexpr (FMT == kFmtFp8) {
-            // 16-lane group gg reads tokens 16kh + 8(gg>>1) + 0..7 x dims
-            // 32db + 16(gg&1) + 0..15; source lane (2r + half) supplies 8 bytes of row r
-            const int gg = lane >> 4, r = c16 >> 1, half = c16 & 1;
-            const uint8_t* src = tb + TL::off(16 * kh + 8 * (gg >> 1) + r, 8 * vb + 2 * db + (gg & 1)) + 8 * half;
-            const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
+            const i32x2 raw = vnext[kh][db];
             va = fp8x8_to_bf16((uint64_t)(uint32_t)raw[0] | ((uint64_t)(uint32_t)raw[1] << 32));
           } else {
-            // two 4-row reads per group: rows 16kh + 8(gg>>1) + 0..3 and + 4..7;
-            // source lane (4r + q) supplies 4 elements of row r
-            const int gg = lane >> 4, r = c16 >> 2, q = c16 & 3;
-            // dims 128vb + 32db + 16(gg&1) + 4q .. +3: chunk 16vb + 4db + 2(gg&1) + q/2, byte 8(q&1)
-            const int row = 16 * kh + 8 * (gg >> 1) + r, chunk = 16 * vb + 4 * db + 2 * (gg & 1) + (q >> 1);
-            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(tb + TL::off(row, chunk) + 8 * (q & 1)));
-            const i16x4 r1 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(tb + TL::off(row + 4, chunk) + 8 * (q & 1)));
-            // whole-vector bit casts: element-wise short -> __bf16 casts of this
-            // result were mis-lowered (the upper dword was dropped)
-            const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
-            const i32x2 a1 = __builtin_bit_cast(i32x2, r1);
-            const i32x4 packed = {a0[0], a0[1], a1[0], a1[1]};
-            va = __builtin_bit_cast(bf16x8, packed);
+            va = __builtin_bit_cast(bf16x8, vnext[kh][db]);
           }
           o[db][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[kh], o[db][kh], 0, 0, 0);
         }
@@ -824,6 +897,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
       }
+      if (k < ntiles) read_v(k);
     }
 
     lds_barrier();                    // QK waves have published each half's max and sum
