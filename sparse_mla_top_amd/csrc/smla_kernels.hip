@@ -489,31 +489,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   uint32_t* const ctr = fused ? a.counters + 2 * (2 * b + hg) : nullptr;   // tickets, finished writes
 
   // ---- 1. QK waves: wave q scores heads 16(q&1) .. +15 of the group against
-  // token half q>>1 of every tile; raw Q of those heads (lane column = head)
+  // token half q>>1 of every tile (lane column = head)
   const int hq = wave & 1, mh = (wave >> 1) & 1;
   const int hloc = 16 * hq + c16;                          // head within the group
   const int head = kHpw * hg + hloc;                       // head of the request
-  const uint16_t* qrow = a.q + ((int64_t)b * kHeads + head) * kDqk;
-  bf16x8 qraw[18];
-  if (qk_role) {
-    if constexpr (FMT == kFmtFp8) {
-      // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          qraw[4 * blk + j] = *reinterpret_cast<const bf16x8*>(qrow + 128 * blk + 32 * g + 8 * j);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c)
-        qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
-    }
-#pragma unroll
-    for (int c = 16; c < 18; ++c)
-      qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
-  }
-
-  // ---- 2. index translation, one token per thread (its latency overlaps Q's)
+  // ---- 2. index translation, one token per thread
   {
     const int t = threadIdx.x;
     bool valid = false;
@@ -530,13 +510,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       mask_s[2 * wave + 1] = (uint32_t)(bits >> 32);
     }
   }
-  // Q must have landed before the barrier: the join of the two roles' code
-  // paths would otherwise leave the compiler a pending Q load to wait for in
-  // the PV waves too, draining their prefetched tiles.
-  if (qk_role) {
-#pragma unroll
-    for (int c = 0; c < 18; ++c) asm volatile("" : "+v"(qraw[c]));
-  }
   lds_barrier();
 
   // ---- 3. the PV waves issue every tile load (the QK waves never wait on
@@ -551,10 +524,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // at least 4 buffers (fp8 rows: 6; bf16 rows fit only 3 and run unpipelined,
   // tile k scored and finished in iteration k).
   constexpr bool kPipe = kNbuf >= 4;
-  // Only the tiles the first iteration needs go out before it: every
-  // workgroup starts at once, and a deeper first burst would delay everyone's
-  // first tile behind the others' later ones.  The rest follow at its top.
-  const int npre = min(kPipe ? 2 : kAhead, ntiles);
+  // The first kAhead tiles go out at once (fp8 rows: 4; measured against 2,
+  // 3 and 5: with fewer, tile 2 is issued only when tiles 0 and 1 have landed
+  // and stalls iteration 1; with more, every workgroup's first tiles queue
+  // behind the others' later ones).  The rest follow one per iteration.
+  const int npre = min(kAhead, ntiles);
   auto src_of = [&](int tt) { return tile_src<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile, vwave, lane); };
   auto issue = [&](int tt, const TileSrc& src) {
     issue_tile<FMT>(src, (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), vwave, lane);
@@ -579,6 +553,26 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 
   if (qk_role) {
     // ---------------------------------------------------------------- QK role
+    // Raw Q of this wave's heads, loaded only now: its latency overlaps the
+    // first tiles' (issued by the PV waves after the barrier above) instead of
+    // delaying the index translation those tiles wait for.
+    const uint16_t* qrow = a.q + ((int64_t)b * kHeads + head) * kDqk;
+    bf16x8 qraw[18];
+    if constexpr (FMT == kFmtFp8) {
+      // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qraw[4 * blk + j] = *reinterpret_cast<const bf16x8*>(qrow + 128 * blk + 32 * g + 8 * j);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+    }
+#pragma unroll
+    for (int c = 16; c < 18; ++c)
+      qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
     i32x8 qhi[FMT == kFmtFp8 ? 4 : 1], qlo[FMT == kFmtFp8 ? 4 : 1];
     bf16x8 qb[18];
     float qscale = 1.0f;           // 2^-e_h, folded into the softmax scale
@@ -632,62 +626,76 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     float l_run = 0.f;              // this lane's share of the running sum
     const int row = 16 * mh + c16;  // tile row this lane's K operand comes from
 
-    // Scores are software-pipelined: in iteration k the MFMAs of tile k+1
-    // are issued before the softmax of tile k (whose MFMA results came from
-    // iteration k-1), so the matrix pipe runs under the softmax's VALU and
-    // cross-lane work.  Raw holds one tile's accumulators before the fp8
-    // block scales, which are applied when the tile is finished.
+    // Scores are software-pipelined (fp8 rows): in iteration k the softmax
+    // of tile k runs on raw scores whose MFMAs were issued in iteration k-1,
+    // while the K operands of tile k+1 are read from LDS; the MFMAs of tile
+    // k+1 follow and run into the barrier.  The block scales of tile k are
+    // read ahead of tile k+1's K operands, so the softmax waits for them only.
+    // Raw holds one tile's accumulators before the fp8 block scales.
     struct Raw {
       f32x4 acc[FMT == kFmtFp8 ? 4 : 1];   // [scale block] (fp8 rows only)
       f32x4 sm;                             // rope part (fp8 rows) or the whole score (bf16 rows)
     };
-    auto issue_scores = [&](int kt, Raw& r) {
+    struct KOps {                           // K operands of one tile (fp8 rows)
+      i32x8 ka[4];                          // codes 128blk + 32g .. +31
+      bf16x8 kr[2];                         // rope dims 32c + 8g .. +7
+    };
+    auto read_k = [&](int kt, KOps& o) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+      // codes 128blk + 32g .. +31 = chunks 8blk + 2g, +1
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const i32x4 k0 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g));
+        const i32x4 k1 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g + 1));
+        o.ka[blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+      }
+      // rope dims 32c + 8g .. +7 sit at byte 528 + 2 (32c + 8g): chunk 33 + 4c + g
+#pragma unroll
+      for (int c = 0; c < 2; ++c) o.kr[c] = *reinterpret_cast<const bf16x8*>(tb + TL::off(row, 33 + 4 * c + g));
+    };
+    auto mfma_scores = [&](const KOps& o, Raw& r) {
+      // independent MFMA chains: hi of every block, rope, then lo
       f32x4 sm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+        r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.ka[blk], qhi[blk], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                     0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.kr[c], qb[16 + c], sm, 0, 0, 0);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+        r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.ka[blk], qlo[blk], r.acc[blk], 0, 0, 0, 0, 0, 0);
+      r.sm = sm;
+    };
+    auto issue_scores = [&](int kt, Raw& r) {
       if constexpr (FMT == kFmtBf16) {
+        const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+        f32x4 sm = {0.f, 0.f, 0.f, 0.f};
         // k-slot group g of 32-dim step c: dims 32c + 8g .. +7 = chunk 4c + g
 #pragma unroll
         for (int c = 0; c < 18; ++c)
           sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(tb + TL::off(row, 4 * c + g)),
                                                       qb[c], sm, 0, 0, 0);
+        r.sm = sm;
       } else {
-        i32x8 ka[4];
-        bf16x8 kr[2];
-        // codes 128blk + 32g .. +31 = chunks 8blk + 2g, +1
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          const i32x4 k0 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g));
-          const i32x4 k1 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g + 1));
-          ka[blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-        }
-        // rope dims 32c + 8g .. +7 sit at byte 528 + 2 (32c + 8g): chunk 33 + 4c + g
-#pragma unroll
-        for (int c = 0; c < 2; ++c) kr[c] = *reinterpret_cast<const bf16x8*>(tb + TL::off(row, 33 + 4 * c + g));
-        // independent MFMA chains: hi of every block, rope, then lo
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[blk], qhi[blk], f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[c], qb[16 + c], sm, 0, 0, 0);
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[blk], qlo[blk], r.acc[blk], 0, 0, 0, 0, 0, 0);
+        KOps o;
+        read_k(kt, o);
+        mfma_scores(o, r);
       }
-      r.sm = sm;
+    };
+    // block scales of this lane's tokens 16mh + 4g + i (fp8 rows)
+    auto read_scales = [&](int kt, float4 (&sv)[4]) {
+      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
     };
     // softmax of tile kt from its raw scores; P^T and alpha to LDS
-    auto finish_tile = [&](int kt, bool dry, const Raw& r) {
-      const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
-      const uint32_t vmask = dry ? 0u : mask_s[kt];
+    auto finish_tile = [&](int kt, bool dry, const Raw& r, const float4 (&sv)[4], uint32_t vmask) {
       f32x4 sacc = r.sm;
-      float4 sv[4];                 // block scales of this lane's tokens 16mh + 4g + i
       if constexpr (FMT == kFmtFp8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
+        for (int i = 0; i < 4; ++i)
           sacc[i] += r.acc[0][i] * sv[i].x + r.acc[1][i] * sv[i].y + r.acc[2][i] * sv[i].z + r.acc[3][i] * sv[i].w;
-        }
       }
       // online softmax (log2 domain) over this half; masked slots score -inf
       float p[4];
@@ -743,8 +751,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           if (!dry) lds_barrier();
           issue_scores(0, cur);
         }
-        if (k + 1 < ntiles) issue_scores(k + 1, nxt);
-        finish_tile(dry ? 0 : k, dry, cur);
+        const int kt = dry ? 0 : k;
+        float4 sv[4];
+        read_scales(kt, sv);
+        const uint32_t mask = mask_s[kt];
+        // The K reads and MFMAs of tile k+1 are unconditional so the compiler
+        // can count the LDS reads in flight and let the softmax wait for the
+        // scales alone; after the last tile they read a stale buffer and the
+        // result is dropped.
+        KOps ko;
+        read_k(k + 1, ko);
+        __builtin_amdgcn_sched_barrier(0);   // every read goes out before the softmax waits
+        finish_tile(kt, dry, cur, sv, dry ? 0u : mask);
+        mfma_scores(ko, nxt);
         if (!dry) lds_barrier();
       }
     };
@@ -764,8 +783,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         if (!dry) lds_barrier();
         if (k == ntiles) break;
         Raw r;
-        issue_scores(dry ? 0 : k, r);
-        finish_tile(dry ? 0 : k, dry, r);
+        const int kt = dry ? 0 : k;
+        issue_scores(kt, r);
+        float4 sv[4];
+        if constexpr (FMT == kFmtFp8) read_scales(kt, sv);
+        finish_tile(kt, dry, r, sv, dry ? 0u : mask_s[kt]);
       }
     }
 
