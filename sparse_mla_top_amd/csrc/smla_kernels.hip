@@ -516,9 +516,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // the texture path)
   const int vwave = wave & 3;
   // In iteration k the QK waves start tile k+1 and finish tile k, and the PV
-  // waves accumulate tile k-1; tile k + kAhead is issued at the top of
-  // iteration k into the buffer of tile k - 2 (finished at k - 2, accumulated
-  // at k - 1, so free after the barrier of iteration k).
+  // waves accumulate tile k-1; tile k + kAhead is issued in iteration k
+  // into the buffer of tile k - 2 (finished at k - 2, accumulated at k - 1,
+  // so free after the barrier of iteration k).
   constexpr int kAhead = kNbuf - 2;
   // The QK look-ahead needs tile k+1 issued before iteration k, i.e. a ring of
   // at least 4 buffers (fp8 rows: 6; bf16 rows fit only 3 and run unpipelined,
@@ -537,7 +537,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     for (int tt = 0; tt < npre; ++tt) issue(tt, src_of(tt));
 
   // Top of iteration k: the PV waves wait for their share of the tile the QK
-  // waves start now, then a barrier publishes it; then they issue more tiles.
+  // waves start now, then a barrier publishes it (they issue more tiles later
+  // in the iteration).
   auto wait_tile_loads = [&](int k) {
     const int need = kPipe ? k + 1 : k;   // the tile the QK waves start in iteration k
     const int issued = k == 0 ? npre : min(ntiles, k + kAhead);   // tiles issued so far
@@ -873,13 +874,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     for (int k = 0; k <= ntiles; ++k) {
       wait_tile_loads(k);
       arrive_barrier();
-      if (k == 0) {
-        for (int tt = npre; tt <= kAhead && tt < ntiles; ++tt) issue(tt, src_of(tt));
-        if (kAhead + 1 < ntiles) nsrc = src_of(kAhead + 1);
-      } else if (k + kAhead < ntiles) {
-        issue(k + kAhead, nsrc);
-        if (k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
-      }
       const bool dry = k == 0;
       const int kt = dry ? 0 : k - 1;   // tile accumulated in this iteration
       const int pb = dry ? 1 : kt & 1;
@@ -918,6 +912,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
+      }
+      // Tile k + kAhead goes out after this iteration's MFMAs: each 1 KB
+      // direct-to-LDS instruction is slow to leave the issue queue, and the
+      // MFMAs run meanwhile.  Its buffer held tile k - 2, done with by every
+      // wave before this iteration's barrier.
+      if (k == 0) {
+        for (int tt = npre; tt <= kAhead && tt < ntiles; ++tt) issue(tt, src_of(tt));
+        if (kAhead + 1 < ntiles) nsrc = src_of(kAhead + 1);
+      } else if (k + kAhead < ntiles) {
+        issue(k + kAhead, nsrc);
+        if (k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
       }
       if (k < ntiles) read_v(k);
     }
