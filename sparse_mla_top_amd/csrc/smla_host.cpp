@@ -64,22 +64,29 @@ size_t workspace_for(int B, int nsplit) {
 // and the given merge placement.  One workgroup is resident per CU (its LDS
 // tiles take most of the 160 KiB), so the B * 2 * nsplit workgroups (two head
 // groups per request) run in ceil(B*2*nsplit / cus) dispatch rounds, each as
-// long as the longest split (chunk tiles of 32 tokens).  Splitting adds the merge: in the kernel, one
-// workgroup per request reads every partial (bounded by one CU's memory
-// parallelism); as a separate launch, a launch gap plus a short,
+// long as the longest split (chunk tiles of 32 tokens).  A round starts with
+// every resident workgroup fetching its first tiles and its Q at once, a
+// burst whose size grows with the grid.  Splitting adds the merge: in the
+// kernel, one workgroup per request reads every partial (bounded by one CU's
+// memory parallelism); as a separate launch, a launch gap plus a short,
 // device-wide read.  The constants are fitted to MI355X timings on cold
-// caches.
+// caches (B = 1..80, nsplit = 1..8, both merges).
 double est_time_us(int B, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
-  const double t_start = 8.0;        // launch, translation and first-gather latency per workgroup
-  const double t_tile = 1.0;         // one 32-token tile for 32 heads on one CU
-  const double us_per_mb = 0.09;     // gathered rows and per-split Q reads, device-wide
-  const double t_fused0 = 4.5, t_fused_split = 0.6;   // in-kernel merge: one workgroup reads every partial
-  const double t_sep0 = 3.0, t_sep_split = 0.3;       // combine launch: gap, lse, partial rounds
+  const double t_start = 7.0;        // launch, translation and first-gather latency per workgroup
+  const double us_per_mb_burst = 0.1;   // first tiles and Q of every resident workgroup
+  const double t_tile = 0.9;         // one 32-token tile for 32 heads on one CU
+  const double t_per_split = 0.4;    // per split of a request, within a round
+  const double us_per_mb = 0.03;     // gathered rows and per-split Q reads, device-wide
+  const double t_fused0 = 3.5, t_fused_split = 0.6;   // in-kernel merge: one workgroup reads every partial
+  const double t_sep0 = 2.0, t_sep_split = 0.1;       // combine launch: gap, lse, partial rounds
   const double us_per_mb_part = 0.2;                  // partial bytes written and read back
   const double mb = 1.0 / (1 << 20);
   const int grid = B * kHeadGroups * nsplit;
   const int rounds = (grid + cus - 1) / cus;
-  double t = rounds * (t_start + chunk_tiles * t_tile) +
+  const int first_tiles = chunk_tiles < 4 ? chunk_tiles : 4;
+  const double burst_mb = mb * (double)(grid < cus ? grid : cus) *
+                          ((double)first_tiles * kTile * row_bytes + (double)kHpw * kDqk * 2);
+  double t = rounds * (t_start + us_per_mb_burst * burst_mb + chunk_tiles * t_tile + t_per_split * nsplit) +
              us_per_mb * mb * (double)B * ((double)kTopk * row_bytes + (double)nsplit * kHeads * kDqk * 2);
   if (nsplit > 1) {
     if (merge == SMLA_MERGE_IN_KERNEL)
