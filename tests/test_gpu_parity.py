@@ -125,6 +125,17 @@ def test_q_zero_and_single_token_closed_forms():
     _check(w, plan=4, what="q=0")
 
 
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
+def test_page_table_longer_than_the_staged_part(fmt):
+    """1.5M-token contexts: the page-table row (23,438 entries) is longer than
+    the part the kernel stages in LDS, so tokens on the last pages are looked up
+    in global memory instead."""
+    w = W.build("longpt", 944, fmt, 3, [1_500_000, 1_499_000, 700], fmt, "uniform", compact=True)
+    assert w.max_pages > 22272
+    for ns in (1, 3):
+        _check(w, plan=ns, what=f"page table longer than staged, nsplit={ns} fmt={fmt}")
+
+
 def test_invalid_page_ids_are_masked():
     w = W.build("badpages", 942, 0, 3, [3000, 3000, 3000], W.FMT_FP8, "uniform")
     w.page_table[0, :10] = -5
