@@ -21,6 +21,16 @@
  *     lse[b,h]   = ln sum_t exp(s_t)           (natural log of scaled scores)
  *     no selected token: out = 0, lse = -inf.
  *
+ * Several query tokens per request (q_len = 2..4, e.g. the draft tokens of a
+ * multi-token verify step) share the request's selection: every (query token,
+ * head) row attends over the same selected rows, which are gathered once per
+ * request and split.  The pages trace the split-K structure back to a verify
+ * attention kernel ("The 64-Block Barrier", section "The Smoking Gun") and
+ * name multi-token (MTP) verification ("Inside the Decode Performance
+ * Investigation", section "Task 3") without defining how draft tokens'
+ * selections relate; sharing one selection is the reading taken here.  With
+ * q_len > 1, q, out and lse gain a query-token dimension after the request.
+ *
  * Memory conventions (all pointers are caller-owned):
  *   - Device pointers are marked [device]; they must be valid on the current
  *     HIP device.  Host pointers are marked [host].
@@ -61,7 +71,7 @@ typedef enum {
 /* Return codes. */
 #define SMLA_OK 0
 #define SMLA_ERR_INVALID_ARG (-1)       /* null pointer, negative size, bad enum           */
-#define SMLA_ERR_UNSUPPORTED_SHAPE (-2) /* heads != 64, d != 576/512, topk != 512, page != 64 */
+#define SMLA_ERR_UNSUPPORTED_SHAPE (-2) /* heads != 64, d != 576/512, topk != 512, page != 64, q_len > 4 */
 #define SMLA_ERR_WORKSPACE (-3)         /* workspace NULL or smaller than smla_plan_for says */
 #define SMLA_ERR_PLAN (-4)              /* an override plan outside the supported values    */
 #define SMLA_ERR_HIP (-5)               /* a HIP runtime call failed                        */
@@ -76,6 +86,7 @@ typedef struct {
     int32_t max_pages_per_req; /* >= 1: row stride of page_table                    */
     int32_t kv_format;         /* smla_kv_format                                    */
     int64_t pool_pages;        /* >= 1: pages in kv_pool                            */
+    int32_t q_len;             /* query tokens per request, 1..4 (0 reads as 1)     */
 } smla_shape;
 
 /* Where the split partials are merged (smla_plan.merge). */
@@ -121,7 +132,7 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
 
 /*
  * sparse_mla_decode -- the attention defined at the top of this header.
- *   q          [device] bf16 [B, 64, 576]
+ *   q          [device] bf16 [B, q_len, 64, 576]
  *   kv_pool    [device] u8   [pool_pages * 64 * row_bytes]  (row format = shape->kv_format)
  *   page_table [device] i32  [B, max_pages_per_req]: logical page -> physical page
  *   topk_idx   [device] i32  [B, 512]: logical token positions.  A slot is masked
@@ -131,13 +142,13 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *                              indices count once per slot.
  *   ctx_len    [device] i32  [B]
  *   scale      softmax scale applied to <q, x> (e.g. 1/sqrt(576))
- *   out        [device] bf16 [B, 64, 512]  (round-to-nearest-even from fp32)
- *   lse        [device] fp32 [B, 64]
+ *   out        [device] bf16 [B, q_len, 64, 512]  (round-to-nearest-even from fp32)
+ *   lse        [device] fp32 [B, q_len, 64]
  *   shape      [host]   problem description
  *   plan_or_null [host] NULL = automatic plan; else as for smla_plan_for's override
  *   workspace  [device] scratch of at least the size smla_plan_for reports
  *                        (may be NULL when that size is 0).  It holds the split
- *                        partials and one arrival counter per request: it must be
+ *                        partials and arrival counters per query token: it must be
  *                        zero-filled once before its first use (smla_workspace_init),
  *                        and every successful call leaves the counters at zero again.
  *                        Calls that share a workspace must not overlap in time.
@@ -163,11 +174,11 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
  * sections "Task 1" and "Task 2": one split and one combine kernel per layer).
  *   smla_decode_split takes exactly the arguments of sparse_mla_decode.  With
  *   nsplit = 1 it writes out/lse itself; otherwise it fills the workspace with
- *   per-split partials (for each (request, split) a 128 KB block holding the
- *   64 x 512 fp32 output normalised by that split's own softmax denominator,
- *   in an internal element order that only smla_decode_combine reads; then
- *   fp32 [B, nsplit, 64] lse at the next 256-byte boundary) and leaves out/lse
- *   and the arrival counters alone.
+ *   per-split partials (for each (request, query token, split) a 128 KB block
+ *   holding the 64 x 512 fp32 output normalised by that split's own softmax
+ *   denominator, in an internal element order that only smla_decode_combine
+ *   reads; then fp32 [B * q_len, nsplit, 64] lse at the next 256-byte
+ *   boundary) and leaves out/lse and the arrival counters alone.
  *   smla_decode_combine merges those partials into out/lse; the same shape and
  *   plan must be passed, and it does nothing when the plan has nsplit = 1.
  * Both return as sparse_mla_decode does.

@@ -105,9 +105,19 @@ def gather(q_shape_B: int, topk: int, kv_format: int, kv_pool: np.ndarray, pool_
 def decode(q: np.ndarray, kv_format: int, kv_pool: np.ndarray, pool_pages: int,
            page_table: np.ndarray, topk_idx: np.ndarray, ctx_len: np.ndarray, scale,
            nthreads: int = 0, lib=None):
-    """Attention over the selected rows: (out float64 [B, H, 512], lse float64 [B, H])."""
+    """Attention over the selected rows: (out float64 [B, H, 512], lse float64 [B, H]).
+
+    q may also be [B, q_len, H, 576]: q_len query tokens per request sharing its
+    selection, each (token, head) row attending over the same selected rows;
+    then out is [B, q_len, H, 512] and lse [B, q_len, H].
+    """
     lib = lib or load()
     q = np.ascontiguousarray(q, dtype=np.uint16)
+    if q.ndim == 4:
+        B4, T4, H4, _ = q.shape
+        o, l = decode(q.reshape(B4, T4 * H4, q.shape[3]), kv_format, kv_pool, pool_pages, page_table,
+                      topk_idx, ctx_len, scale, nthreads=nthreads, lib=lib)
+        return o.reshape(B4, T4, H4, o.shape[-1]), l.reshape(B4, T4, H4)
     B, H, dqk = q.shape
     assert dqk == 576
     pt = np.ascontiguousarray(page_table, dtype=np.int32)

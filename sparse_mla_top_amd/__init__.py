@@ -40,7 +40,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("topk", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("max_pages_per_req", ctypes.c_int32), ("kv_format", ctypes.c_int32),
-                ("pool_pages", ctypes.c_int64)]
+                ("pool_pages", ctypes.c_int64), ("q_len", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -99,9 +99,9 @@ def strerror(code: int) -> str:
     return lib().smla_strerror(int(code)).decode()
 
 
-def make_shape(batch: int, kv_format: int, max_pages_per_req: int, pool_pages: int) -> Shape:
+def make_shape(batch: int, kv_format: int, max_pages_per_req: int, pool_pages: int, q_len: int = 1) -> Shape:
     return Shape(int(batch), NUM_HEADS, D_QK, D_V, TOPK, PAGE_SIZE, int(max_pages_per_req),
-                 int(kv_format), int(pool_pages))
+                 int(kv_format), int(pool_pages), int(q_len))
 
 
 def _plan_arg(plan):
@@ -150,10 +150,11 @@ def _check_tensors(shape: Shape, q, kv_pool, page_table, topk_idx, ctx_len, out,
     B = int(shape.batch)
     if B <= 0:
         return
+    Q = B * max(int(shape.q_len), 1)          # query sets (request, query token)
     rb = ROW_BYTES.get(int(shape.kv_format))
-    need = [(q, B * NUM_HEADS * D_QK * 2, "q"), (page_table, B * int(shape.max_pages_per_req) * 4, "page_table"),
+    need = [(q, Q * NUM_HEADS * D_QK * 2, "q"), (page_table, B * int(shape.max_pages_per_req) * 4, "page_table"),
             (topk_idx, B * TOPK * 4, "topk_idx"), (ctx_len, B * 4, "ctx_len"),
-            (out, B * NUM_HEADS * D_V * 2, "out"), (lse, B * NUM_HEADS * 4, "lse")]
+            (out, Q * NUM_HEADS * D_V * 2, "out"), (lse, Q * NUM_HEADS * 4, "lse")]
     if rb is not None:
         need.append((kv_pool, int(shape.pool_pages) * PAGE_SIZE * rb, "kv_pool"))
     for t, nbytes, name in need:
@@ -209,15 +210,19 @@ def decode(q, kv_pool, page_table, topk_idx, ctx_len, scale, *, kv_format: int, 
            out=None, lse=None, plan=None, workspace=None, stream=None):
     """Sparse-MLA decode attention.  Returns (out bf16 [B,64,512], lse fp32 [B,64]).
 
-    q bf16 [B,64,576]; kv_pool uint8 [pool bytes]; page_table int32 [B,max_pages];
+    q bf16 [B,64,576], or [B,q_len,64,576] for q_len query tokens per request
+    sharing its selection (out [B,q_len,64,512], lse [B,q_len,64]);
+    kv_pool uint8 [pool bytes]; page_table int32 [B,max_pages];
     topk_idx int32 [B,512]; ctx_len int32 [B] -- all on the current GPU.
     """
     B = q.shape[0]
-    shape = make_shape(B, kv_format, page_table.shape[1], pool_pages)
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    lead = (B, q_len) if q.dim() == 4 else (B,)
+    shape = make_shape(B, kv_format, page_table.shape[1], pool_pages, q_len)
     if out is None:
-        out = torch.empty((B, NUM_HEADS, D_V), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty(lead + (NUM_HEADS, D_V), dtype=torch.bfloat16, device=q.device)
     if lse is None:
-        lse = torch.empty((B, NUM_HEADS), dtype=torch.float32, device=q.device)
+        lse = torch.empty(lead + (NUM_HEADS,), dtype=torch.float32, device=q.device)
     if workspace is None:
         _, ws = plan_for(shape, plan)
         workspace = new_workspace(ws, q.device)

@@ -15,7 +15,8 @@ using namespace smla;
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kMaxBatch = 1 << 20;     // keeps B * 512 and B * nsplit grids far below 2^31
+constexpr int kMaxBatch = 1 << 20;     // keeps B * q_len * 512 and the grids far below 2^31
+constexpr int kMaxQLen = 4;            // query tokens per request
 std::atomic<int> g_cu_count[kMaxDevices];   // 0 = not queried yet
 
 int device_cus(int* cus) {
@@ -43,16 +44,22 @@ int check_shape(const smla_shape* s) {
   // slot = page * 64 + row must fit in int64 and the pool in the address space
   const int64_t rb = s->kv_format == SMLA_KV_BF16 ? kRowBytesBf16 : kRowBytesFp8;
   if (s->pool_pages > INT64_MAX / (kPage * rb)) return SMLA_ERR_INVALID_ARG;
-  if (s->batch > kMaxBatch) return SMLA_ERR_INVALID_ARG;
+  if (s->q_len < 0) return SMLA_ERR_INVALID_ARG;
+  if (s->q_len > kMaxQLen) return SMLA_ERR_UNSUPPORTED_SHAPE;
+  if ((int64_t)s->batch * (s->q_len > 0 ? s->q_len : 1) > kMaxBatch) return SMLA_ERR_INVALID_ARG;
   return SMLA_OK;
 }
 
+// Query tokens per request (0 reads as 1) and query sets (request, token).
+int q_len_of(const smla_shape* s) { return s->q_len > 0 ? s->q_len : 1; }
+int query_sets(const smla_shape* s) { return s->batch * q_len_of(s); }
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout (nsplit > 1): fp32 partial outputs [B, nsplit, 64, 512],
-// fp32 partial lse [B, nsplit, 64], uint32 counters [B][head group][2]
-// (arrival tickets, finished partial writes); each region starts at a
-// 256-byte boundary.
+// Workspace layout (nsplit > 1), per query set (request, query token), Q sets
+// in all: fp32 partial outputs [Q, nsplit, 64, 512], fp32 partial lse
+// [Q, nsplit, 64], uint32 counters [Q][head group][2] (arrival tickets,
+// finished partial writes); each region starts at a 256-byte boundary.
 size_t ws_part_o_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * kDv * sizeof(float)); }
 size_t ws_part_lse_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * sizeof(float)); }
 size_t workspace_for(int B, int nsplit) {
@@ -62,8 +69,8 @@ size_t workspace_for(int B, int nsplit) {
 
 // Estimated time (us) of one call with `nsplit` splits on `cus` compute units
 // and the given merge placement.  One workgroup is resident per CU (its LDS
-// tiles take most of the 160 KiB), so the B * 2 * nsplit workgroups (two head
-// groups per request) run in ceil(B*2*nsplit / cus) dispatch rounds, each as
+// tiles take most of the 160 KiB), so the B * q_len * 2 * nsplit workgroups
+// (two head groups per query token) run in ceil(B*q_len*2*nsplit / cus) dispatch rounds, each as
 // long as the longest split (chunk tiles of 32 tokens).  A round starts with
 // every resident workgroup fetching its first tiles and its Q at once, a
 // burst whose size grows with the grid.  Splitting adds the merge: in the
@@ -71,7 +78,7 @@ size_t workspace_for(int B, int nsplit) {
 // memory parallelism); as a separate launch, a launch gap plus a short,
 // device-wide read.  The constants are fitted to MI355X timings on cold
 // caches (B = 1..80, nsplit = 1..8, both merges).
-double est_time_us(int B, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
+double est_time_us(int B, int q_len, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
   const double t_start = 7.0;        // launch, translation and first-gather latency per workgroup
   const double us_per_mb_burst = 0.1;   // first tiles and Q of every resident workgroup
   const double t_tile = 0.9;         // one 32-token tile for 32 heads on one CU
@@ -81,18 +88,18 @@ double est_time_us(int B, int nsplit, int chunk_tiles, int cus, int merge, int r
   const double t_sep0 = 2.0, t_sep_split = 0.1;       // combine launch: gap, lse, partial rounds
   const double us_per_mb_part = 0.2;                  // partial bytes written and read back
   const double mb = 1.0 / (1 << 20);
-  const int grid = B * kHeadGroups * nsplit;
+  const int grid = B * q_len * kHeadGroups * nsplit;
   const int rounds = (grid + cus - 1) / cus;
   const int first_tiles = chunk_tiles < 4 ? chunk_tiles : 4;
   const double burst_mb = mb * (double)(grid < cus ? grid : cus) *
                           ((double)first_tiles * kTile * row_bytes + (double)kHpw * kDqk * 2);
   double t = rounds * (t_start + us_per_mb_burst * burst_mb + chunk_tiles * t_tile + t_per_split * nsplit) +
-             us_per_mb * mb * (double)B * ((double)kTopk * row_bytes + (double)nsplit * kHeads * kDqk * 2);
+             us_per_mb * mb * (double)B * ((double)kTopk * row_bytes + (double)q_len * nsplit * kHeads * kDqk * 2);
   if (nsplit > 1) {
     if (merge == SMLA_MERGE_IN_KERNEL)
       t += t_fused0 + t_fused_split * nsplit;
     else
-      t += t_sep0 + t_sep_split * nsplit + us_per_mb_part * mb * 2.0 * B * nsplit * kHeads * kDv * 4.0;
+      t += t_sep0 + t_sep_split * nsplit + us_per_mb_part * mb * 2.0 * B * q_len * nsplit * kHeads * kDv * 4.0;
   }
   return t;
 }
@@ -107,13 +114,13 @@ int smla_row_bytes(int kv_format) {
   return -1;
 }
 
-int smla_version(void) { return 101; }
+int smla_version(void) { return 102; }
 
 const char* smla_strerror(int code) {
   switch (code) {
     case SMLA_OK: return "ok";
     case SMLA_ERR_INVALID_ARG: return "invalid argument";
-    case SMLA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (need 64 heads, d_qk 576, d_v 512, topk 512, page 64)";
+    case SMLA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (need 64 heads, d_qk 576, d_v 512, topk 512, page 64, q_len <= 4)";
     case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
     case SMLA_ERR_PLAN: return "plan override outside the supported values";
     case SMLA_ERR_HIP: return "HIP runtime error";
@@ -153,14 +160,14 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
     if (forced != 0 && ns != forced) continue;
     for (int m = SMLA_MERGE_IN_KERNEL; m <= SMLA_MERGE_SEPARATE; ++m) {
       if (p.merge != SMLA_MERGE_AUTO && m != p.merge) continue;
-      const double t = est_time_us(B > 0 ? B : 1, ns, chunk, slots, m, smla_row_bytes(shape->kv_format));
+      const double t = est_time_us(B > 0 ? B : 1, q_len_of(shape), ns, chunk, slots, m, smla_row_bytes(shape->kv_format));
       if (t < best - 1e-9) { best = t; best_ns = ns; best_merge = m; }
     }
   }
   p.nsplit = best_ns;
   p.merge = p.nsplit > 1 ? best_merge : SMLA_MERGE_AUTO;
   *out = p;
-  *workspace_bytes = workspace_for(B, p.nsplit);
+  *workspace_bytes = workspace_for(query_sets(shape), p.nsplit);
   return SMLA_OK;
 }
 
@@ -178,6 +185,7 @@ struct Prepared {
   SplitArgs split;
   CombineArgs combine;
   int B = 0;
+  int Q = 0;          // query sets (request, query token)
   int nsplit = 1;
   int merge = SMLA_MERGE_AUTO;
   int fmt = 0;
@@ -191,6 +199,7 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   if (!q || !kv_pool || !page_table || !topk_idx || !ctx_len || !out || !lse) return SMLA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
   const int B = shape->batch;
+  const int Q = query_sets(shape);
   smla_plan plan;
   size_t need = 0;
   rc = smla_plan_for(shape, plan_or_null, &plan, &need);
@@ -207,6 +216,7 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   a.ctx_len = ctx_len;
   a.pool_pages = shape->pool_pages;
   a.max_pages = shape->max_pages_per_req;
+  a.q_len = q_len_of(shape);
   a.nsplit = plan.nsplit;
   a.chunk_tiles = (kTiles + plan.nsplit - 1) / plan.nsplit;
   a.scale_log2 = scale * kLog2e;
@@ -217,8 +227,8 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   a.counters = nullptr;
   if (plan.nsplit > 1) {
     a.part_o = (float*)workspace;
-    a.part_lse = (float*)((uint8_t*)workspace + ws_part_o_bytes(B, plan.nsplit));
-    a.counters = (uint32_t*)((uint8_t*)workspace + ws_part_o_bytes(B, plan.nsplit) + ws_part_lse_bytes(B, plan.nsplit));
+    a.part_lse = (float*)((uint8_t*)workspace + ws_part_o_bytes(Q, plan.nsplit));
+    a.counters = (uint32_t*)((uint8_t*)workspace + ws_part_o_bytes(Q, plan.nsplit) + ws_part_lse_bytes(Q, plan.nsplit));
   }
   CombineArgs& c = pr->combine;
   c.part_o = a.part_o;
@@ -227,6 +237,7 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   c.out = (uint16_t*)out;
   c.lse = lse;
   pr->B = B;
+  pr->Q = Q;
   pr->nsplit = plan.nsplit;
   pr->merge = plan.merge;
   pr->fmt = shape->kv_format;
@@ -243,12 +254,12 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
   if (rc || pr.B == 0) return rc;
   if (pr.nsplit > 1 && pr.merge == SMLA_MERGE_SEPARATE) {
     pr.split.counters = nullptr;       // partials only; the combine launch merges them
-    if (launch_split(pr.split, pr.fmt, pr.B * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
-    if (launch_combine(pr.combine, pr.B, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_combine(pr.combine, pr.Q, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
     return SMLA_OK;
   }
   // one launch: the last split of each request merges the partials
-  if (launch_split(pr.split, pr.fmt, pr.B * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 
@@ -261,7 +272,7 @@ int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_ta
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
   pr.split.counters = nullptr;          // partials only; smla_decode_combine merges them
-  if (launch_split(pr.split, pr.fmt, pr.B * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 
@@ -279,11 +290,11 @@ int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, 
   if ((uintptr_t)out & 7) return SMLA_ERR_INVALID_ARG;
   CombineArgs c;
   c.part_o = (const float*)workspace;
-  c.part_lse = (const float*)((const uint8_t*)workspace + ws_part_o_bytes(shape->batch, plan.nsplit));
+  c.part_lse = (const float*)((const uint8_t*)workspace + ws_part_o_bytes(query_sets(shape), plan.nsplit));
   c.nsplit = plan.nsplit;
   c.out = (uint16_t*)out;
   c.lse = lse;
-  if (launch_combine(c, shape->batch, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  if (launch_combine(c, query_sets(shape), (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 

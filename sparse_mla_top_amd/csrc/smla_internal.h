@@ -26,21 +26,23 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 
 struct SplitArgs {
-  const uint16_t* q;           // bf16 [B][64][576]
+  const uint16_t* q;           // bf16 [B][q_len][64][576]
   const uint8_t* pool;
   const int32_t* page_table;   // [B][max_pages]
   const int32_t* topk_idx;     // [B][512]
   const int32_t* ctx_len;      // [B]
   int64_t pool_pages;
   int max_pages;
+  int q_len;                   // query tokens per request (sharing its selection)
   int nsplit;                  // splits per request
   int chunk_tiles;             // tiles per split (last split may hold fewer)
   float scale_log2;            // softmax scale * log2(e)
-  float* part_o;               // [B][nsplit][64][512] normalised partial outputs
-  float* part_lse;             // [B][nsplit][64] natural-log lse of each split
-  uint16_t* out;               // bf16 [B][64][512] (written directly when nsplit == 1)
-  float* lse;                  // [B][64]
-  uint32_t* counters;          // [B][head group][2] tickets / finished writes; non-null: the last split merges
+  // per (request, query token) = "query set" qs = b * q_len + t:
+  float* part_o;               // [qs][nsplit][64][512] normalised partial outputs
+  float* part_lse;             // [qs][nsplit][64] natural-log lse of each split
+  uint16_t* out;               // bf16 [qs][64][512] (written directly when nsplit == 1)
+  float* lse;                  // [qs][64]
+  uint32_t* counters;          // [qs][head group][2] tickets / finished writes; non-null: the last split merges
 };
 
 struct CombineArgs {

@@ -472,21 +472,26 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int c16 = lane & 15;        // column within a 16-wide MFMA tile
   const bool qk_role = wave < 4;
 
-  // work item -> (request, split, head group); the two head groups of one
-  // (request, split) are neighbours, so they run on one XCD and the second
-  // gathers its rows from that XCD's L2
+  // work item -> (request, split, query token, head group).  The q_len query
+  // tokens of a request share its selected rows; all 2 * q_len workgroups of
+  // one (request, split) are neighbours, so they run on one XCD and all but
+  // the first gather the rows from that XCD's L2.  `vr` = (request, query
+  // token) indexes everything per query (Q, out, lse, partials, counters);
+  // `b` indexes the selection (indices, page table, context length).
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int hg = w & 1;
-  const int bs = w >> 1;
+  const int tq = (w >> 1) % a.q_len;
+  const int bs = (w >> 1) / a.q_len;
   const int b = bs / a.nsplit;
   const int s = bs - b * a.nsplit;
+  const int vr = b * a.q_len + tq;
   const int tile0 = s * a.chunk_tiles;
   if (tile0 >= kTiles) return;   // empty split (the host never launches one)
   const int ntiles = min(a.chunk_tiles, kTiles - tile0);
   const int ntok = ntiles * kTile;
   const int ctx = a.ctx_len[b];
   const bool fused = a.nsplit > 1 && a.counters != nullptr;   // merge in this launch
-  uint32_t* const ctr = fused ? a.counters + 2 * (2 * b + hg) : nullptr;   // tickets, finished writes
+  uint32_t* const ctr = fused ? a.counters + 2 * (2 * vr + hg) : nullptr;   // tickets, finished writes
 
   // ---- 1. QK waves: wave q scores heads 16(q&1) .. +15 of the group against
   // token half q>>1 of every tile (lane column = head)
@@ -557,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // Raw Q of this wave's heads, loaded only now: its latency overlaps the
     // first tiles' (issued by the PV waves after the barrier above) instead of
     // delaying the index translation those tiles wait for.
-    const uint16_t* qrow = a.q + ((int64_t)b * kHeads + head) * kDqk;
+    const uint16_t* qrow = a.q + ((int64_t)vr * kHeads + head) * kDqk;
     bf16x8 qraw[18];
     if constexpr (FMT == kFmtFp8) {
       // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
@@ -946,15 +951,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     const int ghead = kHpw * hg + l32;
     if (vb == 0 && kg == 0) {
       lsev_s[l32] = lse_v;
-      if (a.nsplit == 1) a.lse[(int64_t)b * kHeads + ghead] = lse_v;
-      else if (!(fused && last_s)) store_agent(a.part_lse + ((int64_t)b * a.nsplit + s) * kHeads + ghead, lse_v);
+      if (a.nsplit == 1) a.lse[(int64_t)vr * kHeads + ghead] = lse_v;
+      else if (!(fused && last_s)) store_agent(a.part_lse + ((int64_t)vr * a.nsplit + s) * kHeads + ghead, lse_v);
     }
     // register j of o[db][*] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head l32]
     f32x16 res[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) res[db] = o[db][0] * f[0] + o[db][1] * f[1];
     if (a.nsplit == 1) {
-      uint16_t* orow = a.out + ((int64_t)b * kHeads + ghead) * kDv + 128 * vb + 4 * kg;
+      uint16_t* orow = a.out + ((int64_t)vr * kHeads + ghead) * kDv + 128 * vb + 4 * kg;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -964,7 +969,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
           *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
         }
     } else if (!fused || !last_s) {
-      const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)b * a.nsplit + s) * (kHeads * kDv), kPartBytes);
+      const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)vr * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -1009,9 +1014,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     ctr[1] = 0u;
   }
   lds_barrier();
-  merge_fused(a.part_o, a.part_lse, a.nsplit, b, hg, s, smem, lsev_s, a.out, a.lse,
+  merge_fused(a.part_o, a.part_lse, a.nsplit, vr, hg, s, smem, lsev_s, a.out, a.lse,
               reinterpret_cast<float*>(rowaddr_s));
-  if (fail_s && threadIdx.x < kHpw) a.lse[(int64_t)b * kHeads + kHpw * hg + threadIdx.x] = __builtin_nanf("");
+  if (fail_s && threadIdx.x < kHpw) a.lse[(int64_t)vr * kHeads + kHpw * hg + threadIdx.x] = __builtin_nanf("");
 }
 
 // ----------------------------------------------------------------------------

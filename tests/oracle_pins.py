@@ -329,9 +329,36 @@ def pin_head_and_request_order(lib):
     assert np.array_equal(out2, out[perm][:, hperm]) and np.array_equal(lse2, lse[perm][:, hperm])
 
 
+def pin_query_tokens_share_selection(lib):
+    """q_len query tokens per request: each (token, head) row attends over the
+    request's selected rows, checked against torch SDPA (float64) on the rows
+    gathered here, and against one single-token call per token."""
+    base = W.build("mtp", 913, 0, 3, [9000, 700, 40], W.FMT_FP8, "uniform")
+    w = W.with_query_tokens(base, 3)
+    assert w.q.shape == (3, 3, W.H, W.D_QK) and np.array_equal(w.q[:, 0], base.q)
+    pool = w.host_pool()
+    out, lse = oracle.decode_workload(w, lib=lib, pool=pool)
+    assert out.shape == (3, 3, W.H, 512) and lse.shape == (3, 3, W.H)
+    q = torch.from_numpy(w.q.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+    for b in range(w.B):
+        k, v = _torch_rows(w.kv_format, _valid_rows(w, pool, b))
+        for t in range(3):
+            qb = q[b, t][None, :, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qb, k[None, None].expand(1, W.H, -1, -1), v[None, None].expand(1, W.H, -1, -1),
+                scale=float(w.scale))[0, :, 0, :].numpy()
+            ref_lse = torch.logsumexp(float(w.scale) * (q[b, t] @ k.T), dim=1).numpy()
+            assert np.abs(out[b, t] - ref).max() <= TOL * max(1.0, np.abs(ref).max()), (b, t)
+            assert np.abs(lse[b, t] - ref_lse).max() <= TOL * 10, (b, t)
+    for t in range(3):
+        o1, l1 = oracle.decode(w.q[:, t], w.kv_format, pool, w.pool_pages, w.page_table, w.topk_idx,
+                               w.ctx_len, w.scale, lib=lib)
+        assert np.array_equal(o1, out[:, t]) and np.array_equal(l1, lse[:, t])
+
+
 ALL_PINS = [
     pin_e4m3_all_codes, pin_bf16_all_patterns, pin_gather_bruteforce, pin_dense_equals_sdpa,
     pin_single_token, pin_q_zero, pin_two_tokens, pin_permutation_and_mask_invariance,
     pin_page_relabel, pin_scale_doubling, pin_split_merge, pin_empty_selection,
-    pin_bruteforce_tiny, pin_head_and_request_order,
+    pin_bruteforce_tiny, pin_head_and_request_order, pin_query_tokens_share_selection,
 ]

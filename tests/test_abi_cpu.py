@@ -58,7 +58,8 @@ def _decode_rc(shape, nonnull=True, scale=1 / 24):
     ("d_v", 576, smla.ERR_UNSUPPORTED_SHAPE), ("topk", 2048, smla.ERR_UNSUPPORTED_SHAPE),
     ("page_size", 16, smla.ERR_UNSUPPORTED_SHAPE), ("batch", -1, smla.ERR_INVALID_ARG),
     ("max_pages_per_req", 0, smla.ERR_INVALID_ARG), ("pool_pages", 0, smla.ERR_INVALID_ARG),
-    ("kv_format", 5, smla.ERR_INVALID_ARG),
+    ("kv_format", 5, smla.ERR_INVALID_ARG), ("q_len", 5, smla.ERR_UNSUPPORTED_SHAPE),
+    ("q_len", -1, smla.ERR_INVALID_ARG),
 ])
 def test_shape_validation(field, value, code):
     assert _decode_rc(_shape(**{field: value})) == code
@@ -152,3 +153,22 @@ def test_forced_merge_placement_is_kept(merge):
     # nothing to merge with one split
     p, ws = smla.plan_for_cus(_shape(batch=8), 256, {"nsplit": 1, "merge": merge})
     assert (p.nsplit, p.merge, ws) == (1, 0, 0)
+
+
+def test_query_tokens_scale_the_workspace_and_grid():
+    """q_len query tokens per request: partials and counters per (request,
+    token); q_len = 0 reads as 1; the selector sees q_len times the workgroups."""
+    for ns in (2, 4):
+        ws = {}
+        for q in (0, 1, 2, 3, 4):
+            s = _shape(batch=6, q_len=q)
+            _, ws[q] = smla.plan_for_cus(s, 256, {"nsplit": ns})
+        assert ws[0] == ws[1]
+        a256 = lambda x: (x + 255) // 256 * 256
+        for q in (1, 2, 3, 4):
+            Q = 6 * q
+            assert ws[q] == a256(Q * ns * 64 * 512 * 4) + a256(Q * ns * 64 * 4) + a256(Q * 2 * 2 * 4)
+    # more query tokens never ask for more splits (the grid already fills more of the device)
+    for B in (1, 4, 16, 32):
+        picks = [smla.plan_for_cus(_shape(batch=B, q_len=q), 256)[0].nsplit for q in (1, 2, 3, 4)]
+        assert picks == sorted(picks, reverse=True), (B, picks)

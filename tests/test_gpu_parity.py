@@ -240,3 +240,63 @@ def test_workspace_init_recovers_dirty_counters():
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.decode_workload(w)
     assert_parity(out, lse, ref_o, ref_l, "after workspace_init")
+
+
+# --------------------------------------------------------------- several query tokens per request
+def _mtp_workload(q_len, fmt=W.FMT_FP8):
+    base = W.build("mtp", 950, fmt, 5, [65536, 4096, 700, 300, 131072], fmt, "uniform")
+    return W.with_query_tokens(base, q_len)
+
+
+@pytest.mark.parametrize("q_len", [2, 3, 4])
+def test_query_tokens_share_selection(q_len):
+    w = _mtp_workload(q_len)
+    _check(w, what=f"q_len={q_len} auto plan")
+    for ns in (1, 2, 5):
+        for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
+            _check(w, plan={"nsplit": ns, "merge": merge}, what=f"q_len={q_len} nsplit={ns} merge={merge}")
+
+
+def test_query_tokens_bf16_rows():
+    w = W.with_query_tokens(W.make(1), 4)
+    for ns in (1, 4):
+        _check(w, plan=ns, what=f"q_len=4 bf16 nsplit={ns}")
+
+
+def test_query_tokens_equal_single_token_calls():
+    """Each query token's rows are computed exactly as in a single-token call
+    with the same plan (bit-identical), and the two-stage form matches too."""
+    w = _mtp_workload(3)
+    d = upload(w)
+    for ns in (1, 3):
+        plan = {"nsplit": ns, "merge": smla.MERGE_IN_KERNEL}
+        out, lse = _run(d, plan)
+        for t in range(3):
+            o1, l1 = smla.decode(d.q[:, t].contiguous(), d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale,
+                                 kv_format=d.kv_format, pool_pages=d.pool_pages, plan=plan)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, out[:, t]) and torch.equal(l1, lse[:, t]), f"nsplit={ns} token {t}"
+    shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages, 3)
+    plan, ws_bytes = smla.plan_for(shape, 4)
+    ws = smla.new_workspace(ws_bytes)
+    o_a = torch.empty((w.B, 3, 64, 512), dtype=torch.bfloat16, device="cuda")
+    l_a = torch.empty((w.B, 3, 64), dtype=torch.float32, device="cuda")
+    o_b, l_b = torch.empty_like(o_a), torch.empty_like(l_a)
+    assert smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o_a, l_a, shape,
+                           {"nsplit": 4, "merge": smla.MERGE_IN_KERNEL}, ws) == 0
+    assert smla.split_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o_b, l_b, shape, 4, ws) == 0
+    assert smla.combine_raw(shape, 4, ws, o_b, l_b) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+
+
+def test_query_tokens_masked_and_degenerate():
+    idx = np.full((4, W.TOPK), -1, np.int32)
+    rng = np.random.default_rng(13)
+    idx[1, 7] = 3                                      # one valid token
+    idx[2] = rng.permutation(W.TOPK).astype(np.int32)  # dense ctx = 512
+    idx[3, 480:] = rng.choice(3000, 32, replace=False) # only the last tile valid
+    base = W.build("mtp_degenerate", 951, 0, 4, [1000, 8, 512, 3000], W.FMT_FP8, "given", topk_idx=idx)
+    w = W.with_query_tokens(base, 2)
+    for ns in (1, 4, 16):
+        _check(w, plan=ns, what=f"q_len=2 degenerate nsplit={ns}")

@@ -116,7 +116,7 @@ def lazy_zeros(nbytes: int) -> np.ndarray:
 class Workload:
     name: str
     kv_format: int
-    q: np.ndarray            # uint16 bf16 bits [B, H, 576]
+    q: np.ndarray            # uint16 bf16 bits [B, H, 576], or [B, q_len, H, 576]
     page_table: np.ndarray   # int32 [B, max_pages]
     topk_idx: np.ndarray     # int32 [B, TOPK]
     ctx_len: np.ndarray      # int32 [B]
@@ -128,6 +128,10 @@ class Workload:
     @property
     def B(self) -> int:
         return int(self.q.shape[0])
+
+    @property
+    def q_len(self) -> int:
+        return int(self.q.shape[1]) if self.q.ndim == 4 else 1
 
     @property
     def row_bytes(self) -> int:
@@ -168,6 +172,22 @@ class Workload:
 def _streams(workload_id: int, layer: int):
     ss = np.random.SeedSequence([SEED_BASE, workload_id, layer])
     return [np.random.default_rng(s) for s in ss.spawn(5)]   # q, kv, idx, page table, ctx
+
+
+def with_query_tokens(w: "Workload", q_len: int, seed_tag: int = 0x4D5450) -> "Workload":
+    """A copy of `w` with q_len query tokens per request sharing its selection:
+    q becomes [B, q_len, H, 576]; token 0 is w's own Q, tokens 1.. are N(0,1)
+    draws (bf16 RNE) from the stream SeedSequence([SEED_BASE, seed_tag, name
+    hash, q_len]).  The selection, page table and rows are w's."""
+    assert w.q.ndim == 3 and q_len >= 1
+    B = w.q.shape[0]
+    tag = int.from_bytes(w.name.encode()[:8].ljust(8, b"\0"), "little") & 0x7FFFFFFF
+    rng = np.random.default_rng(np.random.SeedSequence([SEED_BASE, seed_tag, tag, q_len]))
+    q = np.empty((B, q_len, H, D_QK), dtype=np.uint16)
+    q[:, 0] = w.q
+    if q_len > 1:
+        q[:, 1:] = bf16_bits(rng.standard_normal((B, q_len - 1, H, D_QK), dtype=np.float32))
+    return dataclasses.replace(w, q=q, name=f"{w.name}_q{q_len}")
 
 
 def _uniform_idx(rng, ctx: int) -> np.ndarray:
