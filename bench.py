@@ -41,6 +41,8 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, vendor figure
 KERNEL_NAME = "split_kernel<1>"  # fp8 instantiation: the only kernel of a call
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_fp8_b80_ctx128k_traffic.json")
 SWEEP_B = (1, 8, 16, 32, 48, 64, 80, 88, 96)
+MTP_Q_LEN = (2, 4)
+MTP_B = (32, 80)
 LAYERS_PER_STEP = 42
 
 
@@ -57,19 +59,21 @@ def algorithmic(w):
 
     Bytes read: every valid selected row (656 B fp8 / 1152 B bf16), the
     distinct page-table entries it needs, the top-k list, ctx_len and Q
-    (64 x 576 bf16 per request).  Bytes written: out (64 x 512 bf16) and lse
-    (64 fp32) per request.  Split-K partials are not counted: they are this
-    implementation's overhead, not the method's.
-    Flops: per valid (request, head, row) 2*576 for QK^T and 2*512 for PV.
+    (64 x 576 bf16 per request and query token).  Bytes written: out
+    (64 x 512 bf16) and lse (64 fp32) per request and query token.  Split-K
+    partials are not counted: they are this implementation's overhead, not
+    the method's.  With several query tokens the rows are counted once.
+    Flops: per valid (request, query token, head, row) 2*576 for QK^T and
+    2*512 for PV.
     """
     i = w.topk_idx.astype(np.int64)
     valid = (i >= 0) & (i < w.ctx_len[:, None])
     n_valid = int(valid.sum())
     pages = sum(len(np.unique(i[b][valid[b]] // 64)) for b in range(w.B))
-    B = w.B
-    rd = n_valid * w.row_bytes + 4 * pages + 4 * 512 * B + 4 * B + B * 64 * 576 * 2
-    wr = B * 64 * 512 * 2 + B * 64 * 4
-    flops = n_valid * 64 * (2 * 576 + 2 * 512)
+    B, T = w.B, w.q_len
+    rd = n_valid * w.row_bytes + 4 * pages + 4 * 512 * B + 4 * B + B * T * 64 * 576 * 2
+    wr = B * T * (64 * 512 * 2 + 64 * 4)
+    flops = n_valid * T * 64 * (2 * 576 + 2 * 512)
     return int(rd + wr), int(flops)
 
 
@@ -85,6 +89,7 @@ def main() -> int:
     ap.add_argument("--sweep-layers", type=int, default=4)
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mtp", action="store_true", help="skip the several-query-tokens pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -179,6 +184,40 @@ def main() -> int:
             traffic = t.get("hbm_bytes_per_launch")
             traffic_note = t.get("note", "")
 
+    # ------------------------------------------------------------------ query tokens
+    # q_len query tokens per request sharing its selection, on the same cold
+    # input sets (extra Q per token; the rows are those of the headline sets)
+    mtp = None
+    if not args.no_mtp:
+        t2 = time.time()
+        mtp = {}
+        for T in MTP_Q_LEN:
+            qs = [torch.from_numpy(W.with_query_tokens(w, T).q).to(dev).view(torch.bfloat16) for w, _ in sets]
+            per = {}
+            for Bm in MTP_B:
+                shp = smla.make_shape(Bm, w0.kv_format, w0.max_pages, pool_pages, T)
+                pl, wsb = smla.plan_for(shp)
+                w_s = smla.new_workspace(wsb, dev)
+                o = torch.empty((Bm, T, 64, 512), dtype=torch.bfloat16, device=dev)
+                l_ = torch.empty((Bm, T, 64), dtype=torch.float32, device=dev)
+
+                def mcall(k):
+                    d = sets[k % L][1]
+                    rc = smla.decode_raw(qs[k % L][:Bm], d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale,
+                                         o, l_, shp, pl, w_s, stream=stream)
+                    if rc != 0:
+                        raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
+                for k in range(10):
+                    mcall(k)
+                us = statistics.median(timed(mcall, args.sweep_steps) for _ in range(3))
+                byts = float(np.mean([algorithmic(W.with_query_tokens(w.subset(Bm), T))[0] for w, _ in sets[:4]]))
+                per[str(Bm)] = {"us_per_layer": round(us, 2), "us_per_query_token": round(us / T, 2),
+                                "nsplit": pl.nsplit, "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            mtp[str(T)] = per
+            del qs
+        log(f"query-token pass done in {time.time() - t2:.1f}s: {mtp}")
+
     # ------------------------------------------------------------------ B sweep
     sweep = None
     if not args.no_sweep:
@@ -264,6 +303,9 @@ def main() -> int:
             "mfma_frac_bf16_peak": round(call_flops / (full_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4),
             "traffic_note": traffic_note,
             "sweep": sweep,
+            "query_tokens": None if mtp is None else {
+                "workload": w0.name, "q_len": mtp,
+                "note": "q_len query tokens per request share its selection; same 16 cold input sets"},
         },
         "roofline": {"kernel": KERNEL_NAME, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
