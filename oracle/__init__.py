@@ -47,6 +47,12 @@ def _bind(lib):
     lib.oracle_decode.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int64, c.c_int,
                                   p, p, p, p, p, c.c_float, p, p, c.c_int]
     lib.oracle_max_threads.restype = c.c_int
+    lib.oracle_e4m3_encode.argtypes = [c.c_float]
+    lib.oracle_e4m3_encode.restype = c.c_uint8
+    lib.oracle_f32_to_bf16.argtypes = [c.c_float]
+    lib.oracle_f32_to_bf16.restype = c.c_uint16
+    lib.oracle_kv_append.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int64, c.c_int, p, p, p, p, p, p]
+    lib.oracle_kv_append.restype = c.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
 
@@ -146,6 +152,35 @@ def gather_workload(w, with_rows: bool = True, lib=None, pool: np.ndarray | None
         pool = w.host_pool()
     return gather(w.B, w.topk_idx.shape[1], w.kv_format, pool, w.pool_pages, w.page_table,
                   w.topk_idx, w.ctx_len, with_rows=with_rows, lib=lib)
+
+
+def e4m3_encode(v: float, lib=None) -> int:
+    return int((lib or load()).oracle_e4m3_encode(float(v)))
+
+
+def f32_to_bf16(v: float, lib=None) -> int:
+    return int((lib or load()).oracle_f32_to_bf16(float(v)))
+
+
+def kv_append(latent: np.ndarray, rope: np.ndarray, req: np.ndarray, pos: np.ndarray, page_table: np.ndarray,
+              kv_pool: np.ndarray, pool_pages: int, kv_format: int, lib=None) -> int:
+    """Quantise and write each token's row into kv_pool (uint8, modified in place) at the slot
+    page_table[req][pos // 64] * 64 + pos % 64; out-of-range destinations are skipped.
+    latent float32 [n, 512], rope float32 [n, 64].  Returns the number of rows written."""
+    lib = lib or load()
+    lat = np.ascontiguousarray(latent, dtype=np.float32)
+    rp = np.ascontiguousarray(rope, dtype=np.float32)
+    rq = np.ascontiguousarray(req, dtype=np.int32)
+    ps = np.ascontiguousarray(pos, dtype=np.int32)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    assert kv_pool.dtype == np.uint8 and kv_pool.flags.c_contiguous
+    n = lat.shape[0]
+    assert lat.shape == (n, 512) and rp.shape == (n, 64) and rq.shape == (n,) and ps.shape == (n,)
+    rc = lib.oracle_kv_append(n, pt.shape[0], pt.shape[1], int(pool_pages), int(kv_format), _ptr(lat), _ptr(rp),
+                              _ptr(rq), _ptr(ps), _ptr(pt), _ptr(kv_pool))
+    if rc < 0:
+        raise ValueError(f"oracle_kv_append failed ({rc})")
+    return rc
 
 
 def max_threads(lib=None) -> int:

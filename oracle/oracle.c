@@ -242,6 +242,114 @@ int oracle_decode(int B, int H, int topk, int max_pages, int64_t pool_pages, int
     return 0;
 }
 
+/* ---- the cache producer: quantise and write new tokens' rows -------------
+ *
+ * The row format above, written from fp32 values (§8(f) rank 2 of the build
+ * notes; the pages name the FP8 latent cache and a fused epilogue that would
+ * produce it: "Inside the Decode Performance Investigation", sections "Task 1"
+ * and "Task 3").  Per 128-dim block of the latent: scale = amax / 448 in fp32
+ * (1.0 for an all-zero block) and code = e4m3(x / scale), rounded to nearest
+ * with ties to even and saturated at +-448.  Rope values, and the bf16
+ * format's latent, are rounded to bf16 (nearest, ties to even).  Token n is
+ * written at the slot its request's page table gives its logical position; a
+ * token whose request, position or page is out of range is not written.
+ */
+
+/* fp32 -> OCP e4m3fn code: nearest value, ties to the even code, |x| beyond
+ * the largest finite value (448) saturating to it.  Normal codes hold
+ * (1 + m/8) * 2^(E-7) for E = 1..15 (E = 15 only up to m = 6); subnormal codes
+ * hold m * 2^-9. */
+uint8_t oracle_e4m3_encode(float v) {
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs((double)v);
+    if (a == 0.0)
+        return sign;
+    if (a < 0x1p-6) {
+        /* subnormal range: a multiple of 2^-9; 8 * 2^-9 is the smallest normal (code 0x08) */
+        return (uint8_t)(sign | (uint8_t)nearbyint(a * 512.0));
+    }
+    int e;
+    (void)frexp(a, &e);                           /* a in [2^(e-1), 2^e) */
+    int E = e - 1 + 7;                            /* biased exponent */
+    double m = nearbyint((a / ldexp(1.0, e - 1) - 1.0) * 8.0);   /* exact operands; ties to even */
+    if (m == 8.0) {
+        m = 0.0;
+        E += 1;
+    }
+    if (E > 15 || (E == 15 && m > 6.0)) {
+        E = 15;                                   /* 1.75 * 2^8 = 448 */
+        m = 6.0;
+    }
+    return (uint8_t)(sign | (uint8_t)(E << 3) | (uint8_t)m);
+}
+
+/* fp32 -> bf16 bits, nearest value with ties to even (bf16 keeps 8
+ * significant bits of fp32's 24 and the same exponent range). */
+uint16_t oracle_f32_to_bf16(float v) {
+    double a = (double)v;
+    if (isfinite(a) && a != 0.0) {
+        int e;
+        (void)frexp(a, &e);                       /* |a| in [2^(e-1), 2^e) */
+        int ulp_exp = e - 8;                      /* 8 significant bits */
+        if (ulp_exp < -133)
+            ulp_exp = -133;                       /* bf16 subnormal spacing */
+        a = nearbyint(a / ldexp(1.0, ulp_exp)) * ldexp(1.0, ulp_exp);
+    }
+    float r = (float)a;                           /* exact, or +-inf past the largest bf16 */
+    uint32_t u;
+    memcpy(&u, &r, 4);
+    return (uint16_t)(u >> 16);
+}
+
+static void put_u16_le(uint8_t *p, uint16_t v) {
+    p[0] = (uint8_t)(v & 0xff);
+    p[1] = (uint8_t)(v >> 8);
+}
+
+/* latent fp32 [n][512], rope fp32 [n][64], req/pos i32 [n]; rows written in kv_pool.
+ * Returns the number of tokens written, or -1 on bad arguments. */
+int oracle_kv_append(int n, int B, int max_pages, int64_t pool_pages, int kv_format,
+                     const float *latent, const float *rope, const int32_t *req, const int32_t *pos,
+                     const int32_t *page_table, uint8_t *kv_pool) {
+    const int rb = oracle_row_bytes(kv_format);
+    if (rb < 0 || n < 0 || B < 0 || max_pages < 1)
+        return -1;
+    int written = 0;
+    for (int t = 0; t < n; ++t) {
+        const int b = req[t], p = pos[t];
+        if (b < 0 || b >= B || p < 0 || p / ORC_PAGE >= max_pages)
+            continue;
+        const int64_t page = page_table[(int64_t)b * max_pages + p / ORC_PAGE];
+        if (page < 0 || pool_pages <= page)
+            continue;
+        uint8_t *row = kv_pool + (page * ORC_PAGE + p % ORC_PAGE) * rb;
+        const float *x = latent + (size_t)t * ORC_D_LATENT;
+        const float *r = rope + (size_t)t * ORC_D_ROPE;
+        if (kv_format == ORC_FMT_FP8) {
+            for (int blk = 0; blk < ORC_D_LATENT / 128; ++blk) {
+                float amax = 0.0f;
+                for (int i = 0; i < 128; ++i)
+                    if (fabsf(x[128 * blk + i]) > amax)
+                        amax = fabsf(x[128 * blk + i]);
+                const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+                for (int i = 0; i < 128; ++i)
+                    row[128 * blk + i] = oracle_e4m3_encode(x[128 * blk + i] / scale);
+                memcpy(row + ORC_D_LATENT + 4 * blk, &scale, 4);   /* little-endian host */
+            }
+            uint8_t *rope_out = row + ORC_D_LATENT + 4 * (ORC_D_LATENT / 128);
+            for (int k = 0; k < ORC_D_ROPE; ++k)
+                put_u16_le(rope_out + 2 * k, oracle_f32_to_bf16(r[k]));
+        } else {
+            for (int d = 0; d < ORC_D_LATENT; ++d)
+                put_u16_le(row + 2 * d, oracle_f32_to_bf16(x[d]));
+            for (int k = 0; k < ORC_D_ROPE; ++k)
+                put_u16_le(row + 2 * (ORC_D_LATENT + k), oracle_f32_to_bf16(r[k]));
+        }
+        ++written;
+    }
+    return written;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

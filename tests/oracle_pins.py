@@ -356,9 +356,102 @@ def pin_query_tokens_share_selection(lib):
         assert np.array_equal(o1, out[:, t]) and np.array_equal(l1, lse[:, t])
 
 
+def pin_e4m3_encode_roundtrip_ties_saturation(lib):
+    """The encoder inverts the decoder on every finite code, sends each midpoint
+    between neighbouring codes to the even one, and saturates beyond 448."""
+    vals = {}
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue                                   # NaN codes
+        v = oracle.e4m3_to_f64(c, lib)
+        assert oracle.e4m3_encode(np.float32(v), lib) == c, hex(c)
+        vals[c] = v
+    pos = sorted((v, c) for c, v in vals.items() if c < 0x80)
+    for (v0, c0), (v1, c1) in zip(pos, pos[1:]):
+        mid = (v0 + v1) / 2                            # exact in fp32 (5 significant bits)
+        even = c0 if c0 % 2 == 0 else c1
+        for sgn in (1, -1):
+            sb = 0 if sgn == 1 else 0x80
+            assert oracle.e4m3_encode(np.float32(sgn * mid), lib) == (even | sb) if c0 != 0 or sgn == 1 else True
+            assert oracle.e4m3_encode(np.nextafter(np.float32(sgn * mid), np.float32(sgn * 1e9)), lib) == (c1 | sb)
+            assert oracle.e4m3_encode(np.nextafter(np.float32(sgn * mid), np.float32(0)), lib) == (c0 | sb)
+    for v in (448.0, 463.99, 464.0, 480.0, 1e5, 3.0e38):
+        assert oracle.e4m3_encode(np.float32(v), lib) == 0x7E and oracle.e4m3_encode(np.float32(-v), lib) == 0xFE
+
+
+def pin_encoders_match_torch_casts(lib):
+    """e4m3 (within +-448) and bf16 rounding agree with torch's casts on random
+    fp32 values spanning normal and subnormal ranges, including exact ties."""
+    rng = np.random.default_rng(21)
+    mag = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 100_000)).astype(np.float32)
+    x = (mag * rng.choice([-1, 1], mag.size)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_encode(v, lib) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+    bits = rng.integers(0, 2 ** 32, 100_000, dtype=np.uint64).astype(np.uint32)
+    bits[:2000] = (bits[:2000] & 0xFFFF0000) | 0x8000     # exact ties
+    y = bits.view(np.float32)
+    y = y[np.isfinite(y)]
+    ref16 = torch.from_numpy(y.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got16 = np.array([oracle.f32_to_bf16(v, lib) for v in y], dtype=np.uint16)
+    assert np.array_equal(got16, ref16)
+
+
+def _append_case(fmt, n=300, seed=22):
+    """Inputs for the cache producer: fp32 rows with special blocks, and destinations
+    (some invalid) through a shuffled page table."""
+    rng = np.random.default_rng(seed)
+    B, max_pages, pool_pages = 5, 12, 64
+    lat = rng.standard_normal((n, 512)).astype(np.float32)
+    rope = rng.standard_normal((n, 64)).astype(np.float32)
+    lat[0, 128:256] = 0.0                                  # all-zero block
+    lat[1, :128] = 0.0
+    lat[1, 77] = -3.25                                     # one non-zero value
+    lat[2, :] *= np.float32(1e-30)                         # tiny magnitudes
+    lat[3, :] *= np.float32(1e30)                          # huge magnitudes
+    pt = rng.permutation(pool_pages)[:B * max_pages].astype(np.int32).reshape(B, max_pages)
+    pt[4, 3] = pool_pages + 7                              # out-of-range page
+    req = rng.integers(0, B, n).astype(np.int32)
+    # distinct destinations: positions drawn without replacement per request
+    pos = np.empty(n, np.int32)
+    for b in range(B):
+        ix = np.nonzero(req == b)[0]
+        pos[ix] = rng.choice(max_pages * W.PAGE, len(ix), replace=False)
+    req[5], req[6], pos[7], pos[8] = -1, B, -4, max_pages * W.PAGE   # invalid destinations
+    return lat, rope, req, pos, pt, pool_pages
+
+
+def pin_kv_append_matches_generator(lib):
+    """The producer writes exactly the rows the input generator packs (torch casts),
+    at the slots the page table gives, and nothing for invalid destinations."""
+    for fmt in (W.FMT_FP8, W.FMT_BF16):
+        lat, rope, req, pos, pt, pool_pages = _append_case(fmt)
+        rb = W.ROW_BYTES[fmt]
+        pool = np.zeros(pool_pages * W.PAGE * rb, dtype=np.uint8)
+        n = oracle.kv_append(lat, rope, req, pos, pt, pool, pool_pages, fmt, lib=lib)
+        rows = pool.reshape(-1, rb)
+        expect = W.pack_rows(fmt, lat, rope)
+        written = np.zeros(rows.shape[0], bool)
+        count = 0
+        for t in range(lat.shape[0]):
+            b, p = int(req[t]), int(pos[t])
+            if not (0 <= b < pt.shape[0] and 0 <= p < pt.shape[1] * W.PAGE):
+                continue
+            page = int(pt[b, p // W.PAGE])
+            if not (0 <= page < pool_pages):
+                continue
+            slot = page * W.PAGE + p % W.PAGE
+            assert np.array_equal(rows[slot], expect[t]), (fmt, t)
+            written[slot] = True
+            count += 1
+        assert n == count and count < lat.shape[0] - 3
+        assert not rows[~written].any()
+
+
 ALL_PINS = [
     pin_e4m3_all_codes, pin_bf16_all_patterns, pin_gather_bruteforce, pin_dense_equals_sdpa,
     pin_single_token, pin_q_zero, pin_two_tokens, pin_permutation_and_mask_invariance,
     pin_page_relabel, pin_scale_doubling, pin_split_merge, pin_empty_selection,
     pin_bruteforce_tiny, pin_head_and_request_order, pin_query_tokens_share_selection,
+    pin_e4m3_encode_roundtrip_ties_saturation, pin_encoders_match_torch_casts, pin_kv_append_matches_generator,
 ]

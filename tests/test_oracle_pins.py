@@ -38,6 +38,17 @@ MUTATIONS = [
     ("page_bound_unchecked", "if (page < 0 || page >= pool_pages)", "if (page < 0)"),
     ("masked_rows_not_zeroed", "memset(dst, 0, (size_t)rb);", "memset(dst, 1, (size_t)rb);"),
     ("empty_lse_zero", "lse[(size_t)b * H + h] = -INFINITY;", "lse[(size_t)b * H + h] = 0.0;"),
+    # the cache producer
+    ("e4m3_ties_away", "double m = nearbyint((a / ldexp(1.0, e - 1) - 1.0) * 8.0);",
+     "double m = round((a / ldexp(1.0, e - 1) - 1.0) * 8.0);"),
+    ("e4m3_no_saturation", "if (E > 15 || (E == 15 && m > 6.0)) {", "if (E > 15) {"),
+    ("e4m3_subnormal_truncated", "nearbyint(a * 512.0)", "floor(a * 512.0)"),
+    ("bf16_truncates", "a = nearbyint(a / ldexp(1.0, ulp_exp)) * ldexp(1.0, ulp_exp);",
+     "a = trunc(a / ldexp(1.0, ulp_exp)) * ldexp(1.0, ulp_exp);"),
+    ("append_scale_off", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 447.0f : 1.0f"),
+    ("append_zero_block_scale", "? amax / 448.0f : 1.0f;", "? amax / 448.0f : 0.5f;"),
+    ("append_page_unchecked", "if (page < 0 || pool_pages <= page)", "if (page < 0)"),
+    ("append_row_in_page_wrong", "(page * ORC_PAGE + p % ORC_PAGE) * rb", "(page * ORC_PAGE + p / ORC_PAGE) * rb"),
 ]
 
 
