@@ -204,6 +204,31 @@ int smla_gather_rows(const void* kv_pool, const int32_t* page_table, const int32
                      void* stream);
 
 /*
+ * smla_kv_append -- the cache producer: quantise n_tokens new tokens' rows and
+ * write them into the paged cache in the row format this library reads (the
+ * pages name the FP8 latent cache the decode gathers from, "Inside the Decode
+ * Performance Investigation", section "Task 1", and a hand-fused epilogue that
+ * would produce it, section "Task 3").
+ *   latent     [device] fp32 [n_tokens, 512], 16-byte aligned
+ *   rope       [device] fp32 [n_tokens, 64], 16-byte aligned
+ *   req        [device] i32  [n_tokens]: request of each token, in [0, shape->batch)
+ *   pos        [device] i32  [n_tokens]: its logical position in that request
+ *   page_table [device] i32  [B, max_pages_per_req], as for sparse_mla_decode
+ *   kv_pool    [device] u8   pool; row page_table[req][pos / 64] * 64 + pos % 64 is written
+ *   shape      [host]   batch, max_pages_per_req, pool_pages and kv_format are used
+ * Row contents: fp8 format -- per 128-dim block j, scale_j = amax / 448 in fp32
+ * (1.0 for an all-zero block) and code = e4m3fn(x / scale_j), nearest with ties
+ * to even, saturated at +-448; then the 4 scales (fp32 little-endian) and the
+ * rope values as bf16.  bf16 format -- latent then rope as bf16.  bf16 values
+ * are rounded to nearest, ties to even.  A token whose request, position or page
+ * is out of range is skipped; two tokens with one destination leave either row.
+ * Only the destination rows are written.  Returns as sparse_mla_decode does.
+ */
+int smla_kv_append(const float* latent, const float* rope, const int32_t* req, const int32_t* pos,
+                   const int32_t* page_table, void* kv_pool, int32_t n_tokens, const smla_shape* shape,
+                   void* stream);
+
+/*
  * smla_workspace_init -- zero a workspace (its arrival counters) on `stream`
  * with a fill kernel, before its first use by sparse_mla_decode, or after a
  * call that did not complete.  workspace [device], 4-byte aligned.

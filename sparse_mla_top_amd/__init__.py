@@ -85,6 +85,8 @@ def lib():
         L.smla_workspace_init.restype = ctypes.c_int
         L.smla_gather_rows.argtypes = [vp, i32p, i32p, i32p, ctypes.POINTER(Shape), vp, i64p, vp]
         L.smla_gather_rows.restype = ctypes.c_int
+        L.smla_kv_append.argtypes = [vp, vp, i32p, i32p, i32p, vp, ctypes.c_int32, ctypes.POINTER(Shape), vp]
+        L.smla_kv_append.restype = ctypes.c_int
         L.smla_row_bytes.argtypes = [ctypes.c_int]
         L.smla_row_bytes.restype = ctypes.c_int
         L.smla_strerror.argtypes = [ctypes.c_int]
@@ -244,3 +246,29 @@ def gather_rows(kv_pool, page_table, topk_idx, ctx_len, *, kv_format: int, pool_
     if rc != OK:
         raise SmlaError(rc, "smla_gather_rows")
     return rows, slots
+
+
+def kv_append_raw(latent, rope, req, pos, page_table, kv_pool, shape: Shape, stream=None) -> int:
+    """smla_kv_append on torch tensors; returns the library's status code."""
+    n = int(latent.shape[0]) if latent is not None else 0
+    if n > 0:
+        for t, nbytes, name in ((latent, n * 512 * 4, "latent"), (rope, n * 64 * 4, "rope"), (req, n * 4, "req"),
+                                (pos, n * 4, "pos"),
+                                (page_table, int(shape.batch) * int(shape.max_pages_per_req) * 4, "page_table")):
+            have = t.numel() * t.element_size()
+            if have < nbytes or not t.is_contiguous():
+                raise ValueError(f"{name}: {have} bytes (contiguous={t.is_contiguous()}) but {nbytes} are needed")
+        rb = ROW_BYTES.get(int(shape.kv_format))
+        if rb is not None and kv_pool.numel() * kv_pool.element_size() < int(shape.pool_pages) * PAGE_SIZE * rb:
+            raise ValueError("kv_pool is smaller than shape.pool_pages pages")
+    return lib().smla_kv_append(_ptr(latent), _ptr(rope), _ptr(req), _ptr(pos), _ptr(page_table), _ptr(kv_pool),
+                                n, ctypes.byref(shape), _stream(stream))
+
+
+def kv_append(latent, rope, req, pos, page_table, kv_pool, *, kv_format: int, pool_pages: int, stream=None) -> None:
+    """Quantise new tokens' rows (latent fp32 [n,512], rope fp32 [n,64]) and write them into
+    kv_pool at page_table[req][pos // 64] * 64 + pos % 64 (all on the current GPU)."""
+    shape = make_shape(page_table.shape[0], kv_format, page_table.shape[1], pool_pages)
+    rc = kv_append_raw(latent, rope, req, pos, page_table, kv_pool, shape, stream)
+    if rc != OK:
+        raise SmlaError(rc, "smla_kv_append")

@@ -298,6 +298,30 @@ int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, 
   return SMLA_OK;
 }
 
+int smla_kv_append(const float* latent, const float* rope, const int32_t* req, const int32_t* pos,
+                   const int32_t* page_table, void* kv_pool, int32_t n_tokens, const smla_shape* shape,
+                   void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (n_tokens < 0) return SMLA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return SMLA_OK;
+  if (!latent || !rope || !req || !pos || !page_table || !kv_pool) return SMLA_ERR_INVALID_ARG;
+  if (((uintptr_t)latent & 15) || ((uintptr_t)rope & 15) || ((uintptr_t)kv_pool & 15)) return SMLA_ERR_INVALID_ARG;
+  AppendArgs a;
+  a.latent = latent;
+  a.rope = rope;
+  a.req = req;
+  a.pos = pos;
+  a.page_table = page_table;
+  a.pool = (uint8_t*)kv_pool;
+  a.pool_pages = shape->pool_pages;
+  a.batch = shape->batch;
+  a.max_pages = shape->max_pages_per_req;
+  a.n = n_tokens;
+  if (launch_append(a, shape->kv_format, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 int smla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || ((uintptr_t)workspace & 3)) return workspace_bytes == 0 ? SMLA_OK : SMLA_ERR_INVALID_ARG;
   if (launch_zero((uint32_t*)workspace, workspace_bytes / 4, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;

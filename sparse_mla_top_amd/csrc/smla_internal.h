@@ -64,7 +64,21 @@ struct GatherArgs {
   int64_t* slots;
 };
 
+struct AppendArgs {
+  const float* latent;         // fp32 [n][512]
+  const float* rope;           // fp32 [n][64]
+  const int32_t* req;          // [n] request of each new token
+  const int32_t* pos;          // [n] its logical position
+  const int32_t* page_table;   // [batch][max_pages]
+  uint8_t* pool;               // rows written here
+  int64_t pool_pages;
+  int batch;
+  int max_pages;
+  int n;
+};
+
 hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, int fmt, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int fmt, int B, hipStream_t stream);
 hipError_t launch_zero(uint32_t* p, size_t n, hipStream_t stream);

@@ -172,3 +172,15 @@ def test_query_tokens_scale_the_workspace_and_grid():
     for B in (1, 4, 16, 32):
         picks = [smla.plan_for_cus(_shape(batch=B, q_len=q), 256)[0].nsplit for q in (1, 2, 3, 4)]
         assert picks == sorted(picks, reverse=True), (B, picks)
+
+
+def test_kv_append_validation():
+    L = smla.lib()
+    p = ctypes.c_void_p(16)
+    s = _shape()
+    assert L.smla_kv_append(p, p, p, p, p, p, -1, ctypes.byref(s), None) == smla.ERR_INVALID_ARG
+    assert L.smla_kv_append(None, None, None, None, None, None, 0, ctypes.byref(s), None) == smla.OK   # nothing to do
+    assert L.smla_kv_append(None, p, p, p, p, p, 4, ctypes.byref(s), None) == smla.ERR_INVALID_ARG
+    assert L.smla_kv_append(ctypes.c_void_p(20), p, p, p, p, p, 4, ctypes.byref(s), None) == smla.ERR_INVALID_ARG
+    assert L.smla_kv_append(p, p, p, p, p, p, 4, ctypes.byref(_shape(num_heads=8)), None) == smla.ERR_UNSUPPORTED_SHAPE
+    assert L.smla_kv_append(p, p, p, p, p, p, 4, None, None) == smla.ERR_INVALID_ARG
