@@ -42,6 +42,7 @@ KERNEL_NAME = "split_kernel<1>"  # fp8 instantiation: the only kernel of a call
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_fp8_b80_ctx128k_traffic.json")
 SWEEP_B = (1, 8, 16, 32, 48, 64, 80, 88, 96)
 MTP_Q_LEN = (2, 4)
+APPEND_N = (80, 4096, 65536)
 MTP_B = (32, 80)
 LAYERS_PER_STEP = 42
 
@@ -90,6 +91,7 @@ def main() -> int:
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mtp", action="store_true", help="skip the several-query-tokens pass")
+    ap.add_argument("--no-append", action="store_true", help="skip the cache-producer pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -218,6 +220,40 @@ def main() -> int:
             del qs
         log(f"query-token pass done in {time.time() - t2:.1f}s: {mtp}")
 
+    # ------------------------------------------------------------------ cache producer
+    # smla_kv_append writing n new tokens' fp8 rows for 80 requests (token i: request
+    # i % 80, next position) into a separate pool whose pages are a random permutation
+    append = None
+    if not args.no_append:
+        append = {}
+        g = torch.Generator(device=dev).manual_seed(7)
+        for n in APPEND_N:
+            Ba = 80
+            per_req = (n + Ba - 1) // Ba
+            npg = (per_req + W.PAGE - 1) // W.PAGE
+            apool_pages = Ba * npg
+            apool = torch.zeros(apool_pages * W.PAGE * 656, dtype=torch.uint8, device=dev)
+            apt = torch.randperm(apool_pages, generator=g, device=dev).to(torch.int32).view(Ba, npg)
+            lat = torch.randn((n, 512), generator=g, device=dev, dtype=torch.float32)
+            rope = torch.randn((n, 64), generator=g, device=dev, dtype=torch.float32)
+            ar = torch.arange(n, device=dev, dtype=torch.int32)
+            req, pos = (ar % Ba).contiguous(), (ar // Ba).contiguous()
+            ashape = smla.make_shape(Ba, W.FMT_FP8, npg, apool_pages)
+
+            def acall(k):
+                rc = smla.kv_append_raw(lat, rope, req, pos, apt, apool, ashape, stream)
+                if rc != 0:
+                    raise RuntimeError(f"kv_append failed: {smla.strerror(rc)}")
+            for k in range(10):
+                acall(k)
+            us = statistics.median(timed(acall, 200) for _ in range(3))
+            byts = n * (512 * 4 + 64 * 4 + 4 + 4 + 4 + 656)
+            append[str(n)] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                              "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              "algorithmic_bytes": byts}
+            del apool, lat, rope
+        log(f"cache-producer pass: {append}")
+
     # ------------------------------------------------------------------ B sweep
     sweep = None
     if not args.no_sweep:
@@ -303,6 +339,9 @@ def main() -> int:
             "mfma_frac_bf16_peak": round(call_flops / (full_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4),
             "traffic_note": traffic_note,
             "sweep": sweep,
+            "kv_append": None if append is None else {
+                "kernel": "append_kernel<1>", "format": "fp8 rows from fp32 latent/rope", "requests": 80,
+                "per_n_tokens": append},
             "query_tokens": None if mtp is None else {
                 "workload": w0.name, "q_len": mtp,
                 "note": "q_len query tokens per request share its selection; same 16 cold input sets"},
