@@ -285,9 +285,31 @@ def main() -> int:
             us = statistics.median(timed(lambda k: call(subs[k % Ls], shp, pl, w_s, o, l_), args.sweep_steps)
                                    for _ in range(3))
             byts = float(np.mean([algorithmic(w.subset(Bs))[0] for w in full]))
+            # the 42-layer step captured as one HIP graph (layer l reads layer l % Ls's inputs)
+            gs = torch.cuda.Stream()
+            gs.wait_stream(stream)
+            graph = torch.cuda.CUDAGraph()
+
+            def step_on(st):
+                for k in range(LAYERS_PER_STEP):
+                    d = subs[k % Ls]
+                    if smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l_, shp, pl,
+                                       w_s, stream=st) != 0:
+                        raise RuntimeError("decode failed during capture")
+            with torch.cuda.stream(gs):
+                step_on(gs)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=gs):
+                    step_on(gs)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                graph.replay()
+            step_us = statistics.median(timed(lambda k: graph.replay(), 20) for _ in range(3))
+            del graph
             per_b[Bs] = {"us_per_layer": round(us, 2), "nsplit": pl.nsplit,
                          "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                         "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                         "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "graph_step_us_42_layers": round(step_us, 1)}
             del subs
         bs = np.array(SWEEP_B, dtype=float)
         ys = np.array([per_b[b]["us_per_layer"] for b in SWEEP_B])
