@@ -53,6 +53,11 @@ def _bind(lib):
     lib.oracle_f32_to_bf16.restype = c.c_uint16
     lib.oracle_kv_append.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int64, c.c_int, p, p, p, p, p, p]
     lib.oracle_kv_append.restype = c.c_int
+    lib.oracle_topk_select.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int64, p, p, p, p]
+    lib.oracle_topk_select.restype = c.c_int
+    lib.oracle_indexer.argtypes = [c.c_int, c.c_int, c.c_int, c.c_int, c.c_int, c.c_int64, p, p, p, p, p, p, p,
+                                   c.c_int]
+    lib.oracle_indexer.restype = c.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
 
@@ -181,6 +186,42 @@ def kv_append(latent: np.ndarray, rope: np.ndarray, req: np.ndarray, pos: np.nda
     if rc < 0:
         raise ValueError(f"oracle_kv_append failed ({rc})")
     return rc
+
+
+def indexer(q: np.ndarray, w: np.ndarray, kpool: np.ndarray, pool_pages: int, page_table: np.ndarray,
+            ctx_len: np.ndarray, topk: int = 512, nthreads: int = 0, lib=None):
+    """Indexer scores and selection: (scores float64 [B, max_pages*64] (NaN where excluded),
+    topk_idx int32 [B, topk]).  q bf16 bits [B, HI, DI], w float32 [B, HI],
+    kpool bf16 bits [pool_pages*64, DI]."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    kp = np.ascontiguousarray(kpool, dtype=np.uint16)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    B, HI, DI = q.shape
+    scores = np.empty((B, pt.shape[1] * 64), dtype=np.float64)
+    idx = np.empty((B, topk), dtype=np.int32)
+    rc = lib.oracle_indexer(B, HI, DI, topk, pt.shape[1], int(pool_pages), _ptr(q), _ptr(w), _ptr(kp), _ptr(pt),
+                            _ptr(ctx), _ptr(scores), _ptr(idx), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_indexer failed ({rc})")
+    return scores, idx
+
+
+def topk_select(scores: np.ndarray, pool_pages: int, page_table: np.ndarray, ctx_len: np.ndarray, topk: int = 512,
+                lib=None) -> np.ndarray:
+    """The selection rule alone, on given scores [B, max_pages*64] (e.g. a kernel's fp32 scores)."""
+    lib = lib or load()
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_len, dtype=np.int32)
+    idx = np.empty((pt.shape[0], topk), dtype=np.int32)
+    rc = lib.oracle_topk_select(pt.shape[0], topk, pt.shape[1], int(pool_pages), _ptr(pt), _ptr(ctx), _ptr(sc),
+                                _ptr(idx))
+    if rc != 0:
+        raise ValueError(f"oracle_topk_select failed ({rc})")
+    return idx
 
 
 def max_threads(lib=None) -> int:

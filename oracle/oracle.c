@@ -350,6 +350,98 @@ int oracle_kv_append(int n, int B, int max_pages, int64_t pool_pages, int kv_for
     return written;
 }
 
+/* ---- the top-k indexer ------------------------------------------------------
+ *
+ * The step that produces topk_idx.  The pages name the indexer (its launches per
+ * step: "Inside the Decode Performance Investigation", sections "The Setup" and
+ * "Task 2") but give no formula; this follows the published lightning indexer
+ * of DeepSeek's sparse attention, restated (a reading listed in the design
+ * notes): for request b with indexer queries q[j][0..DI) and head weights w[j]
+ * (j < HI), every context position s < ctx_len[b] whose page is valid scores
+ *     I[s] = sum_j w[j] * max(0, sum_d q[j][d] * k_s[d])
+ * with k_s the bf16 key row of s in its own paged cache (same page table as
+ * the latent cache); the selection is the topk valid positions of largest I,
+ * equal scores ordered by smaller s, written in that order, then -1 padding.
+ */
+
+static int topk_cmp_desc(const void *pa, const void *pb) {
+    const double *a = (const double *)pa, *b = (const double *)pb;   /* (score, position) */
+    if (a[0] > b[0]) return -1;
+    if (a[0] < b[0]) return 1;
+    return (a[1] < b[1]) ? -1 : (a[1] > b[1]);
+}
+
+/* The selection rule on given scores [B][max_pages * 64] (only valid positions
+ * are read).  topk_idx [B][topk].  Returns 0, or -1/-2 on bad arguments / memory. */
+int oracle_topk_select(int B, int topk, int max_pages, int64_t pool_pages, const int32_t *page_table,
+                       const int32_t *ctx_len, const double *scores, int32_t *topk_idx) {
+    if (B < 0 || topk < 0 || max_pages < 1)
+        return -1;
+    const int64_t npos = (int64_t)max_pages * ORC_PAGE;
+    double *pairs = (double *)malloc(sizeof(double) * 2 * (size_t)(npos > 0 ? npos : 1));
+    if (!pairs)
+        return -2;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = 0;
+        const int64_t ctx = ctx_len[b] < npos ? ctx_len[b] : npos;
+        for (int64_t s = 0; s < ctx; ++s) {
+            const int64_t page = page_table[(int64_t)b * max_pages + s / ORC_PAGE];
+            if (!(page >= 0 && page < pool_pages))
+                continue;
+            pairs[2 * n] = scores[(int64_t)b * npos + s];
+            pairs[2 * n + 1] = (double)s;
+            ++n;
+        }
+        qsort(pairs, (size_t)n, 2 * sizeof(double), topk_cmp_desc);
+        for (int j = 0; j < topk; ++j)
+            topk_idx[(int64_t)b * topk + j] = j < n ? (int32_t)pairs[2 * j + 1] : -1;
+    }
+    free(pairs);
+    return 0;
+}
+
+/* q bf16 [B][HI][DI], w fp32 [B][HI], kpool bf16 [pool_pages * 64][DI];
+ * scores fp64 [B][max_pages * 64] (valid positions written, others NaN);
+ * topk_idx [B][topk]. */
+int oracle_indexer(int B, int HI, int DI, int topk, int max_pages, int64_t pool_pages,
+                   const uint16_t *q, const float *w, const uint16_t *kpool, const int32_t *page_table,
+                   const int32_t *ctx_len, double *scores, int32_t *topk_idx, int nthreads) {
+    if (B < 0 || HI < 1 || DI < 1 || topk < 0 || max_pages < 1)
+        return -1;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t npos = (int64_t)max_pages * ORC_PAGE;
+    for (int64_t i = 0; i < (int64_t)B * npos; ++i)
+        scores[i] = NAN;
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        double *qd = (double *)malloc(sizeof(double) * (size_t)HI * DI);
+        for (int i = 0; i < HI * DI; ++i)
+            qd[i] = oracle_bf16_to_f64(q[(size_t)b * HI * DI + i]);
+        const int64_t ctx = ctx_len[b] < npos ? ctx_len[b] : npos;
+        for (int64_t s = 0; ctx > s; ++s) {
+            const int64_t page = page_table[(int64_t)b * max_pages + s / ORC_PAGE];
+            if (page >= pool_pages || page < 0)
+                continue;
+            const uint16_t *k = kpool + (page * ORC_PAGE + s % ORC_PAGE) * DI;
+            double acc = 0.0;
+            for (int j = 0; j < HI; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < DI; ++d)
+                    dot += qd[j * DI + d] * oracle_bf16_to_f64(k[d]);
+                acc += (double)w[(size_t)b * HI + j] * (dot > 0.0 ? dot : 0.0);
+            }
+            scores[(int64_t)b * npos + s] = acc;
+        }
+        free(qd);
+    }
+    return oracle_topk_select(B, topk, max_pages, pool_pages, page_table, ctx_len, scores, topk_idx);
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

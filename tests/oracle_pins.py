@@ -448,10 +448,74 @@ def pin_kv_append_matches_generator(lib):
         assert not rows[~written].any()
 
 
+def _bf(bits):
+    return torch.from_numpy(np.asarray(bits).astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def pin_indexer_bruteforce(lib):
+    """Scores and selection against plain Python loops on a small case (4 heads, 8 dims,
+    topk 16, three requests with ragged contexts, one invalid page)."""
+    inp = W.indexer_inputs(3, [300, 9, 130], 1, heads=4, dim=8)
+    inp.page_table[0, 2] = inp.pool_pages + 3                 # positions 128..191 of request 0 excluded
+    sc, idx = oracle.indexer(inp.q, inp.w, inp.keys, inp.pool_pages, inp.page_table, inp.ctx_len, topk=16, lib=lib)
+    q, k = _bf(inp.q), _bf(inp.keys)
+    for b in range(3):
+        pairs = []
+        for s_ in range(int(inp.ctx_len[b])):
+            page = int(inp.page_table[b, s_ // W.PAGE])
+            if not 0 <= page < inp.pool_pages:
+                assert math.isnan(sc[b, s_])
+                continue
+            row = k[page * W.PAGE + s_ % W.PAGE]
+            v = sum(float(inp.w[b, j]) * max(0.0, float(np.dot(q[b, j], row))) for j in range(4))
+            assert abs(sc[b, s_] - v) <= 1e-12 * max(1.0, abs(v))
+            pairs.append((-v, s_))
+        pairs.sort()
+        want = [p_[1] for p_ in pairs[:16]] + [-1] * max(0, 16 - len(pairs))
+        assert list(idx[b]) == want, b
+
+
+def pin_indexer_closed_forms_and_ties(lib):
+    """q = 0 scores every position 0, so the selection is the first valid positions in
+    order; duplicated key rows tie exactly and the smaller position comes first; scaling
+    every weight by 2 doubles every score and keeps the selection; a head whose products
+    are all negative contributes nothing whatever its weight."""
+    inp = W.indexer_inputs(2, [1000, 40], 2, heads=8, dim=16)
+    q0 = np.zeros_like(inp.q)
+    sc0, idx0 = oracle.indexer(q0, inp.w, inp.keys, inp.pool_pages, inp.page_table, inp.ctx_len, topk=64, lib=lib)
+    assert np.all(sc0[0, :1000] == 0) and list(idx0[0]) == list(range(64))
+    assert list(idx0[1]) == list(range(40)) + [-1] * 24
+    # exact ties: copy the key row of position 500 onto positions 700 and 900
+    keys = inp.keys.copy()
+    slot = lambda s_: int(inp.page_table[0, s_ // W.PAGE]) * W.PAGE + s_ % W.PAGE
+    keys[slot(700)] = keys[slot(500)]
+    keys[slot(900)] = keys[slot(500)]
+    sc, idx = oracle.indexer(inp.q, inp.w, keys, inp.pool_pages, inp.page_table, inp.ctx_len, topk=1000, lib=lib)
+    order = list(idx[0])
+    assert sc[0, 500] == sc[0, 700] == sc[0, 900]
+    assert order.index(500) + 1 == order.index(700) and order.index(700) + 1 == order.index(900)
+    sc2, idx2 = oracle.indexer(inp.q, inp.w * np.float32(2), keys, inp.pool_pages, inp.page_table, inp.ctx_len,
+                               topk=1000, lib=lib)
+    ok = ~np.isnan(sc)
+    assert np.array_equal(sc2[ok], 2 * sc[ok]) and np.array_equal(idx2, idx)
+    q3 = inp.q.copy()
+    q3[:, 0] = W.bf16_bits(-np.abs(_bf(inp.keys).sum(axis=0)[None, :]).astype(np.float32))   # q_0 . k mostly < 0
+    sc3, _ = oracle.indexer(q3, inp.w, keys, inp.pool_pages, inp.page_table, inp.ctx_len, topk=8, lib=lib)
+    w4 = inp.w.copy()
+    w4[:, 0] = 123.0
+    sc4, _ = oracle.indexer(q3, w4, keys, inp.pool_pages, inp.page_table, inp.ctx_len, topk=8, lib=lib)
+    qq, kk = _bf(q3), _bf(keys)
+    for b, s_ in ((0, 10), (0, 999), (1, 5)):
+        row = kk[int(inp.page_table[b, s_ // W.PAGE]) * W.PAGE + s_ % W.PAGE]
+        if float(np.dot(qq[b, 0], row)) < 0:
+            assert sc3[b, s_] == sc4[b, s_]
+
+
 ALL_PINS = [
     pin_e4m3_all_codes, pin_bf16_all_patterns, pin_gather_bruteforce, pin_dense_equals_sdpa,
     pin_single_token, pin_q_zero, pin_two_tokens, pin_permutation_and_mask_invariance,
     pin_page_relabel, pin_scale_doubling, pin_split_merge, pin_empty_selection,
     pin_bruteforce_tiny, pin_head_and_request_order, pin_query_tokens_share_selection,
     pin_e4m3_encode_roundtrip_ties_saturation, pin_encoders_match_torch_casts, pin_kv_append_matches_generator,
+    pin_indexer_bruteforce, pin_indexer_closed_forms_and_ties,
 ]

@@ -49,6 +49,13 @@ MUTATIONS = [
     ("append_zero_block_scale", "? amax / 448.0f : 1.0f;", "? amax / 448.0f : 0.5f;"),
     ("append_page_unchecked", "if (page < 0 || pool_pages <= page)", "if (page < 0)"),
     ("append_row_in_page_wrong", "(page * ORC_PAGE + p % ORC_PAGE) * rb", "(page * ORC_PAGE + p / ORC_PAGE) * rb"),
+    # the top-k indexer
+    ("indexer_relu_dropped", "(dot > 0.0 ? dot : 0.0)", "dot"),
+    ("indexer_tie_order_reversed", "return (a[1] < b[1]) ? -1 : (a[1] > b[1]);", "return (a[1] > b[1]) ? -1 : (a[1] < b[1]);"),
+    ("indexer_weight_dropped", "acc += (double)w[(size_t)b * HI + j] * ", "acc += 1.0 * "),
+    ("indexer_padding_zero", ": -1;", ": 0;"),
+    ("indexer_select_page_unchecked", "if (!(page >= 0 && page < pool_pages))", "if (page < 0)"),
+    ("indexer_ctx_inclusive", "for (int64_t s = 0; s < ctx; ++s) {", "for (int64_t s = 0; s <= ctx && s < npos; ++s) {"),
 ]
 
 

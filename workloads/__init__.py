@@ -302,3 +302,40 @@ def make(workload_id: int, layer: int = 0, compact: bool | None = None, page_bas
         return build(name, 5, layer, 96, [524288] * 96, FMT_FP8 if kv_format is None else kv_format,
                      "uniform", True if compact is None else compact, page_base)
     raise ValueError(workload_id)
+
+# --------------------------------------------------------------------------- indexer inputs
+INDEXER_HEADS = 64
+INDEXER_DIM = 128
+
+
+@dataclasses.dataclass
+class IndexerInputs:
+    q: np.ndarray            # uint16 bf16 bits [B, HI, DI]
+    w: np.ndarray            # float32 [B, HI]
+    keys: np.ndarray         # uint16 bf16 bits [pool_pages * 64, DI]
+    page_table: np.ndarray   # int32 [B, max_pages]
+    ctx_len: np.ndarray      # int32 [B]
+    pool_pages: int
+
+
+def indexer_inputs(B: int, ctx_len, seed: int, heads: int = INDEXER_HEADS, dim: int = INDEXER_DIM,
+                   max_pages: int | None = None) -> IndexerInputs:
+    """Seeded inputs of the top-k indexer: q ~ N(0,1) and keys ~ N(0,1) rounded to bf16,
+    head weights ~ U(-0.25, 1) (mostly positive), every logical page of every request on a
+    distinct physical page (a random permutation of the pool).  Stream:
+    SeedSequence([SEED_BASE, 0x1D3, seed])."""
+    rng = np.random.default_rng(np.random.SeedSequence([SEED_BASE, 0x1D3, seed]))
+    ctx = np.asarray(ctx_len, dtype=np.int64).reshape(B)
+    npages = (ctx + PAGE - 1) // PAGE
+    mp = int(max(1, npages.max())) if max_pages is None else max_pages
+    pool_pages = int(max(1, npages.sum()))
+    perm = rng.permutation(pool_pages)
+    pt = np.zeros((B, mp), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        pt[b, :npages[b]] = perm[off:off + npages[b]]
+        off += int(npages[b])
+    q = bf16_bits(rng.standard_normal((B, heads, dim), dtype=np.float32))
+    w = rng.uniform(-0.25, 1.0, (B, heads)).astype(np.float32)
+    keys = bf16_bits(rng.standard_normal((pool_pages * PAGE, dim), dtype=np.float32))
+    return IndexerInputs(q=q, w=w, keys=keys, page_table=pt, ctx_len=ctx.astype(np.int32), pool_pages=pool_pages)
