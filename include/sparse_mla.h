@@ -229,6 +229,34 @@ int smla_kv_append(const float* latent, const float* rope, const int32_t* req, c
                    void* stream);
 
 /*
+ * smla_indexer_topk -- the top-k indexer: produce the topk_idx that
+ * sparse_mla_decode reads.  The pages name the indexer ("Inside the Decode
+ * Performance Investigation", sections "The Setup" and "Task 2") without a
+ * formula; this computes the published lightning indexer of DeepSeek's sparse
+ * attention: for request b and every position s < ctx_len[b] whose page is
+ * valid (as for sparse_mla_decode),
+ *     score[b][s] = sum_j head_w[b][j] * max(0, <q_idx[b][j], k_s>)   (j < 64 heads)
+ * with k_s the bf16 key row of s, and selects the 512 valid positions of largest
+ * score (equal scores: smaller s first), in that order, then -1 padding.
+ *   q_idx      [device] bf16 [B, 64, 128], 16-byte aligned
+ *   head_w     [device] fp32 [B, 64]
+ *   key_pool   [device] bf16 [pool_pages * 64, 128]: one 256-B key row per slot,
+ *                        16-byte aligned, paged by `page_table` like kv_pool
+ *   page_table [device] i32  [B, max_pages_per_req]; ctx_len [device] i32 [B]
+ *   scores     [device] fp32 [B, max_pages_per_req * 64]: written with each valid
+ *                        position's fp32 score (-inf where its page is invalid;
+ *                        positions >= ctx_len untouched); the selection is made on
+ *                        these values
+ *   topk_idx   [device] i32  [B, 512]
+ *   shape      [host]   batch, max_pages_per_req and pool_pages are used
+ * Two launches on `stream` (scores, then one selecting workgroup per request).
+ * Returns as sparse_mla_decode does.
+ */
+int smla_indexer_topk(const void* q_idx, const float* head_w, const void* key_pool, const int32_t* page_table,
+                      const int32_t* ctx_len, float* scores, int32_t* topk_idx, const smla_shape* shape,
+                      void* stream);
+
+/*
  * smla_workspace_init -- zero a workspace (its arrival counters) on `stream`
  * with a fill kernel, before its first use by sparse_mla_decode, or after a
  * call that did not complete.  workspace [device], 4-byte aligned.

@@ -87,6 +87,8 @@ def lib():
         L.smla_gather_rows.restype = ctypes.c_int
         L.smla_kv_append.argtypes = [vp, vp, i32p, i32p, i32p, vp, ctypes.c_int32, ctypes.POINTER(Shape), vp]
         L.smla_kv_append.restype = ctypes.c_int
+        L.smla_indexer_topk.argtypes = [vp, vp, vp, i32p, i32p, vp, i32p, ctypes.POINTER(Shape), vp]
+        L.smla_indexer_topk.restype = ctypes.c_int
         L.smla_row_bytes.argtypes = [ctypes.c_int]
         L.smla_row_bytes.restype = ctypes.c_int
         L.smla_strerror.argtypes = [ctypes.c_int]
@@ -272,3 +274,39 @@ def kv_append(latent, rope, req, pos, page_table, kv_pool, *, kv_format: int, po
     rc = kv_append_raw(latent, rope, req, pos, page_table, kv_pool, shape, stream)
     if rc != OK:
         raise SmlaError(rc, "smla_kv_append")
+
+
+INDEXER_HEADS = 64
+INDEXER_DIM = 128
+
+
+def indexer_topk_raw(q_idx, head_w, key_pool, page_table, ctx_len, scores, topk_idx, shape: Shape,
+                     stream=None) -> int:
+    """smla_indexer_topk on torch tensors; returns the library's status code."""
+    B = int(shape.batch)
+    if B > 0:
+        npos = int(shape.max_pages_per_req) * PAGE_SIZE
+        for t, nbytes, name in ((q_idx, B * INDEXER_HEADS * INDEXER_DIM * 2, "q_idx"),
+                                (head_w, B * INDEXER_HEADS * 4, "head_w"),
+                                (key_pool, int(shape.pool_pages) * PAGE_SIZE * INDEXER_DIM * 2, "key_pool"),
+                                (page_table, B * int(shape.max_pages_per_req) * 4, "page_table"),
+                                (ctx_len, B * 4, "ctx_len"), (scores, B * npos * 4, "scores"),
+                                (topk_idx, B * TOPK * 4, "topk_idx")):
+            have = t.numel() * t.element_size()
+            if have < nbytes or not t.is_contiguous():
+                raise ValueError(f"{name}: {have} bytes (contiguous={t.is_contiguous()}) but {nbytes} are needed")
+    return lib().smla_indexer_topk(_ptr(q_idx), _ptr(head_w), _ptr(key_pool), _ptr(page_table), _ptr(ctx_len),
+                                   _ptr(scores), _ptr(topk_idx), ctypes.byref(shape), _stream(stream))
+
+
+def indexer_topk(q_idx, head_w, key_pool, page_table, ctx_len, *, pool_pages: int, stream=None):
+    """Top-k indexer: returns (topk_idx int32 [B,512], scores fp32 [B,max_pages*64]).
+    q_idx bf16 [B,64,128]; head_w fp32 [B,64]; key_pool bf16 [pool_pages*64,128]."""
+    B, mp = page_table.shape
+    shape = make_shape(B, KV_FP8, mp, pool_pages)
+    scores = torch.empty((B, mp * PAGE_SIZE), dtype=torch.float32, device=q_idx.device)
+    idx = torch.empty((B, TOPK), dtype=torch.int32, device=q_idx.device)
+    rc = indexer_topk_raw(q_idx, head_w, key_pool, page_table, ctx_len, scores, idx, shape, stream)
+    if rc != OK:
+        raise SmlaError(rc, "smla_indexer_topk")
+    return idx, scores

@@ -322,6 +322,29 @@ int smla_kv_append(const float* latent, const float* rope, const int32_t* req, c
   return SMLA_OK;
 }
 
+int smla_indexer_topk(const void* q_idx, const float* head_w, const void* key_pool, const int32_t* page_table,
+                      const int32_t* ctx_len, float* scores, int32_t* topk_idx, const smla_shape* shape,
+                      void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (shape->batch == 0) return SMLA_OK;
+  if (!q_idx || !head_w || !key_pool || !page_table || !ctx_len || !scores || !topk_idx) return SMLA_ERR_INVALID_ARG;
+  if (((uintptr_t)q_idx & 15) || ((uintptr_t)key_pool & 15)) return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)shape->max_pages_per_req * kPage > INT32_MAX / 2) return SMLA_ERR_INVALID_ARG;
+  IndexerArgs a;
+  a.q = (const uint16_t*)q_idx;
+  a.w = head_w;
+  a.keys = (const uint8_t*)key_pool;
+  a.page_table = page_table;
+  a.ctx_len = ctx_len;
+  a.scores = scores;
+  a.topk = topk_idx;
+  a.pool_pages = shape->pool_pages;
+  a.max_pages = shape->max_pages_per_req;
+  if (launch_indexer(a, shape->batch, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 int smla_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || ((uintptr_t)workspace & 3)) return workspace_bytes == 0 ? SMLA_OK : SMLA_ERR_INVALID_ARG;
   if (launch_zero((uint32_t*)workspace, workspace_bytes / 4, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
