@@ -92,6 +92,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mtp", action="store_true", help="skip the several-query-tokens pass")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer pass")
+    ap.add_argument("--no-indexer", action="store_true", help="skip the top-k indexer pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -254,6 +255,44 @@ def main() -> int:
             del apool, lat, rope
         log(f"cache-producer pass: {append}")
 
+    # ------------------------------------------------------------------ top-k indexer
+    # smla_indexer_topk for 80 requests with 131072-token contexts: every call
+    # streams the whole 2.7 GB key cache (pages a random permutation of the pool)
+    indexer = None
+    if not args.no_indexer:
+        t3 = time.time()
+        g = torch.Generator(device=dev).manual_seed(11)
+        Bi, ctx_i = 80, 131072
+        mp = ctx_i // W.PAGE
+        ipool_pages = Bi * mp
+        keys = torch.randn((ipool_pages * W.PAGE, 128), generator=g, device=dev, dtype=torch.bfloat16)
+        ipt = torch.randperm(ipool_pages, generator=g, device=dev).to(torch.int32).view(Bi, mp).contiguous()
+        qi = torch.randn((Bi, 64, 128), generator=g, device=dev, dtype=torch.bfloat16)
+        wi = torch.rand((Bi, 64), generator=g, device=dev, dtype=torch.float32) * 1.25 - 0.25
+        ctxi = torch.full((Bi,), ctx_i, dtype=torch.int32, device=dev)
+        isc = torch.empty((Bi, mp * W.PAGE), dtype=torch.float32, device=dev)
+        iidx = torch.empty((Bi, 512), dtype=torch.int32, device=dev)
+        ishape = smla.make_shape(Bi, W.FMT_FP8, mp, ipool_pages)
+
+        def icall(k):
+            rc = smla.indexer_topk_raw(qi, wi, keys, ipt, ctxi, isc, iidx, ishape, stream)
+            if rc != 0:
+                raise RuntimeError(f"indexer failed: {smla.strerror(rc)}")
+        for k in range(3):
+            icall(k)
+        us = statistics.median(timed(icall, 20) for _ in range(3))
+        pages = Bi * mp
+        byts = Bi * ctx_i * (128 * 2 + 4) + 4 * pages + Bi * (64 * 128 * 2 + 64 * 4 + 4 + 512 * 4)
+        flops = Bi * ctx_i * 64 * 128 * 2
+        indexer = {"kernel": "indexer_score_kernel + indexer_select_kernel", "B": Bi, "ctx_len": ctx_i,
+                   "heads": 64, "head_dim": 128, "key_format": "bf16", "us": round(us, 2),
+                   "algorithmic_bytes": int(byts), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "mfma_frac_bf16_peak": round(flops / (us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+        del keys, ipt, qi, wi, isc, iidx
+        torch.cuda.empty_cache()
+        log(f"indexer pass done in {time.time() - t3:.1f}s: {indexer}")
+
     # ------------------------------------------------------------------ B sweep
     sweep = None
     if not args.no_sweep:
@@ -361,6 +400,7 @@ def main() -> int:
             "mfma_frac_bf16_peak": round(call_flops / (full_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4),
             "traffic_note": traffic_note,
             "sweep": sweep,
+            "indexer_topk": indexer,
             "kv_append": None if append is None else {
                 "kernel": "append_kernel<1>", "format": "fp8 rows from fp32 latent/rope", "requests": 80,
                 "per_n_tokens": append},

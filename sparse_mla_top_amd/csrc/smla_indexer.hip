@@ -11,15 +11,19 @@
 // its own paged cache (same page table as the latent cache); the selection is
 // the 512 largest I (equal scores: smaller s first), in that order, then -1.
 //
-//   score kernel  : one wave per 64 positions; key rows stream from HBM straight
-//                   into bf16 16x16x32 MFMAs against Q held in registers, and the
-//                   ReLU-weighted head sum is a 16-lane butterfly.  HBM-bound:
-//                   256 B read and 4 B written per position.
-//   select kernel : one 1024-thread workgroup per request; a three-pass radix
-//                   select (12 + 12 + 8 bits) on order-preserving keys finds the
-//                   512th score exactly, one ordered pass collects the winners
-//                   (ties by position), and a bitonic sort orders them.
+//   score kernel  : one wave per 1024 positions; key rows stream from HBM
+//                   into a per-wave LDS ring four tiles ahead and feed bf16
+//                   16x16x32 MFMAs against Q held in registers; the
+//                   ReLU-weighted head sum is a 16-lane DPP reduction.
+//                   HBM-bound: 256 B read and 4 B written per position.
+//   select kernel : one 1024-thread workgroup per request; the range of the
+//                   valid scores' order-preserving keys is cut into 4096 bins
+//                   (again inside the bin holding the 512th, as needed) until at
+//                   most 4096 candidates remain, which are sorted in LDS by
+//                   score, then position.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "smla_internal.h"
 
@@ -30,9 +34,15 @@ namespace {
 typedef __bf16 ibf16x8 __attribute__((ext_vector_type(8)));
 typedef float if32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kIdxWaves = 4;                       // score kernel: 4 waves x 64 positions
-constexpr int kIdxPosPerWg = 64 * kIdxWaves;
+constexpr int kScWaves = 4;                        // score kernel: 4 waves per workgroup
+constexpr int kScRing = 4;                         // key tiles in flight per wave
+constexpr int kScPagesPerWave = 16;                // 1024 positions per wave
+constexpr int kScPosPerWave = kScPagesPerWave * kPage;
+constexpr int kScPosPerWg = kScPosPerWave * kScWaves;
+constexpr int kTileBytes = 16 * kIdxDim * 2;       // 16 key rows
 constexpr int kSelThreads = 1024;                  // select kernel
+constexpr int kMaxPageWords = 4096;                // page-validity bitmask in LDS: up to 131072 pages
+static_assert(kScPagesPerWave <= 64, "page ids are held one per lane");
 
 // Source of key rows that must not be read (invalid page, past the context).
 __device__ __attribute__((aligned(16))) uint8_t g_zero_key[kIdxDim * 2];
@@ -46,17 +56,74 @@ __device__ __forceinline__ bool page_ok(const IndexerArgs& a, int b, int s, int*
   return pg >= 0 && (int64_t)pg < a.pool_pages;
 }
 
-// grid: x = block of 256 positions, y = request b; wave v takes positions
-// 256 blockIdx.x + 64 v .. + 63, as four 16-position MFMA tiles.
-__global__ __launch_bounds__(64 * kIdxWaves) void indexer_score_kernel(IndexerArgs a) {
+// One direct-to-LDS load: 16 bytes per lane from `src` to LDS address
+// lds + 16 * lane.  Inline asm, so the compiler neither orders it against
+// every LDS access nor waits for it: completion is tracked with wait_vm.
+// AFTER_READS first waits for this wave's outstanding LDS reads, for a load
+// that overwrites a slot just read.
+template <bool AFTER_READS>
+__device__ __forceinline__ void lds_load16(const void* src, uint32_t lds) {
+  if constexpr (AFTER_READS)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "m0", "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0", "memory");
+}
+// s_waitcnt vmcnt(N); also a compiler barrier for the LDS reads that follow.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// Wait for a tile when `after` (0 .. K) later tiles, 4 loads each, may stay in
+// flight: vector memory loads complete in issue order.
+template <int K> __device__ __forceinline__ void wait_tile(int after) {
+  if constexpr (K == 0) {
+    wait_vm<0>();
+  } else {
+    if (after >= K) wait_vm<4 * K>();
+    else wait_tile<K - 1>(after);
+  }
+}
+
+// Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15), all lanes
+// receiving the total: pairs of lanes (xor 1, xor 2 within quads), then the
+// mirrored quad in each half-row, then the mirrored half.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+// grid: x = block of 4096 positions, y = request b.  Wave v takes the 16 pages
+// from position 4096 blockIdx.x + 1024 v, as 64 MFMA tiles of 16 positions.
+// Each tile's 4 KB of key rows goes straight to a slot of the wave's own LDS
+// ring (kScRing slots, no other wave touches them), kScRing tiles ahead of the
+// one being scored.
+__global__ __launch_bounds__(64 * kScWaves) void indexer_score_kernel(IndexerArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kScWaves * kScRing * kTileBytes];
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int s_wave = blockIdx.x * kIdxPosPerWg + 64 * wave;
-  const int npos = min(a.ctx_len[b], a.max_pages * kPage);   // positions the row of scores holds
+  const int s_wave = blockIdx.x * kScPosPerWg + kScPosPerWave * wave;
+  const int ctx = a.ctx_len[b];
+  const int npos = min(ctx, a.max_pages * kPage);  // positions the row of scores holds
   if (s_wave >= npos) return;
   const int g = lane >> 4, c16 = lane & 15;
+  const int ntile = min(kScPosPerWave / 16, (npos - s_wave + 15) / 16);
 
+  // lane j < 16: physical page of the wave's page j, -1 when invalid
+  int pgv = -1;
+  {
+    const int lp = s_wave / kPage + lane;
+    if (lane < kScPagesPerWave && lp < a.max_pages) {
+      const int pg = a.page_table[(int64_t)b * a.max_pages + lp];
+      pgv = pg >= 0 && (int64_t)pg < a.pool_pages ? pg : -1;
+    }
+  }
   // Q as the MFMA B operand: head block hb (16 heads), k-step ks (32 dims):
   // lane holds q[16 hb + c16][32 ks + 8 g .. + 7]
   const uint16_t* qb = a.q + (int64_t)b * kIdxHeads * kIdxDim;
@@ -70,16 +137,41 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_score_kernel(IndexerAr
       qv[hb][ks] = *reinterpret_cast<const ibf16x8*>(qb + (16 * hb + c16) * kIdxDim + 32 * ks + 8 * g);
   }
 
+  // tile: 16 key rows, 4 KB contiguous within a page.  Load j reads rows
+  // 4j .. 4j+3 as one contiguous KB: lane L takes row r = 4j + L / 16, 16-byte
+  // chunk (L % 16) ^ r, so that in LDS row r holds its chunk c at
+  // slot + 256 r + 16 (c ^ r); the swizzle keeps the MFMA operand reads below
+  // (16 rows, one chunk each) on distinct banks.
+  uint8_t* const mine = ring + wave * kScRing * kTileBytes;
+  const uint32_t mine_lds = (uint32_t)(uintptr_t)mine;
+  auto issue = [&](int tile, auto after_reads) {
+    const int page = __builtin_amdgcn_readlane(pgv, tile >> 2);
+    const uint32_t dst = mine_lds + (tile % kScRing) * kTileBytes;
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb) {
-    // K as the MFMA A operand: lane holds key[s = s_wave + 16 pb + c16][32 ks + 8 g .. + 7]
-    const int s = s_wave + 16 * pb + c16;
-    int page = 0;
-    const bool ok = page_ok(a, b, s, &page);
-    const uint8_t* krow = ok ? a.keys + ((int64_t)page * kPage + (s & (kPage - 1))) * (kIdxDim * 2) : g_zero_key;
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      const int s = s_wave + 16 * tile + r;
+      const int chunk = (lane & 15) ^ r;
+      const uint8_t* src = page >= 0 && s < ctx
+                               ? a.keys + ((int64_t)page * kPage + (s & (kPage - 1))) * (kIdxDim * 2) + 16 * chunk
+                               : g_zero_key + 16 * chunk;
+      if (j == 0) lds_load16<decltype(after_reads)::value>(src, dst);
+      else lds_load16<false>(src, dst + 1024 * j);
+    }
+  };
+  const int npre = min(kScRing, ntile);
+  for (int i = 0; i < npre; ++i) issue(i, std::false_type{});
+
+  float keep = 0.f;                                // this lane's score in the current page
+#pragma unroll 1
+  for (int tile = 0; tile < ntile; ++tile) {
+    // tiles issued after this one: their 4 loads each may stay in flight
+    wait_tile<kScRing - 1>(min(kScRing - 1, ntile - 1 - tile));
+    const uint8_t* slot = mine + (tile % kScRing) * kTileBytes;
     ibf16x8 kv[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kv[ks] = *reinterpret_cast<const ibf16x8*>(krow + 2 * (32 * ks + 8 * g));
+    for (int ks = 0; ks < 4; ++ks) kv[ks] = *reinterpret_cast<const ibf16x8*>(slot + 256 * c16 + 16 * ((4 * ks + g) ^ c16));
+    // A operand, k-step ks: lane (c16, g) holds key[16 tile + c16][32 ks + 8 g .. + 7]
     // S[16 positions][16 heads] per head block; lane (c16, g) holds positions 4g..4g+3 of head c16
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -90,21 +182,20 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_score_kernel(IndexerAr
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[i] += wv[hb] * fmaxf(acc[i], 0.f);
     }
-    // sum over the 16 heads of each block: the 16 lanes of one row group
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] += __shfl_xor(part[i], m, 16);
-    // lane (c16 = i, g) writes position 16 pb + 4 g + i
-    if (c16 < 4) {
-      const int sp = s_wave + 16 * pb + 4 * g + c16;
-      int pg = 0;
-      float v = part[0];
-      v = c16 == 1 ? part[1] : v;
-      v = c16 == 2 ? part[2] : v;
-      v = c16 == 3 ? part[3] : v;
-      if (sp < npos) a.scores[(int64_t)b * a.max_pages * kPage + sp] = page_ok(a, b, sp, &pg) ? v : -INFINITY;
+    for (int i = 0; i < 4; ++i) part[i] = row16_sum(part[i]);   // over the 16 heads of the block
+    // lane (c16, g) keeps position 16 (c16 / 4) + 4 g + c16 % 4 of the page: from tile c16 / 4
+    const int tt = tile & 3;
+    if ((c16 >> 2) == tt) {
+      const int i = c16 & 3;
+      keep = i == 0 ? part[0] : i == 1 ? part[1] : i == 2 ? part[2] : part[3];
     }
+    if (tt == 3 || tile == ntile - 1) {
+      const int sp = s_wave + 64 * (tile >> 2) + 16 * (c16 >> 2) + 4 * g + (c16 & 3);
+      const bool pv = __builtin_amdgcn_readlane(pgv, tile >> 2) >= 0;
+      if ((c16 >> 2) <= tt && sp < npos) a.scores[(int64_t)b * a.max_pages * kPage + sp] = pv ? keep : -INFINITY;
+    }
+    if (tile + kScRing < ntile) issue(tile + kScRing, std::true_type{});
   }
 }
 
@@ -114,124 +205,272 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block-wide exclusive prefix sum of one 0/1 flag per thread (1024 threads);
+// Block-wide exclusive prefix sum of one int per thread (kSelThreads threads);
 // returns this thread's prefix and writes the block total to *total.
-__device__ __forceinline__ int block_scan(bool flag, int* wave_tot, int* total) {
+__device__ __forceinline__ int block_scan(int v, int* wave_tot, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t m = __builtin_amdgcn_ballot_w64(flag);
-  const int in_wave = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wave_tot[wave] = __builtin_popcountll(m);
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
   for (int w = 0; w < kSelThreads / 64; ++w) {
-    const int t = wave_tot[w];
-    before += w < wave ? t : 0;
-    all += t;
+    const int tw = wave_tot[w];
+    before += w < wave ? tw : 0;
+    all += tw;
   }
   __syncthreads();                                 // wave_tot is reused by the next scan
   *total = all;
-  return before + in_wave;
+  return before + incl - v;
 }
+
+// Wave-level reductions (all lanes receive the result).
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Selection for one request (one 1024-thread workgroup).  The k-th largest key
+// is bracketed, not computed: the range [min, max] of the valid keys is cut into
+// at most 4096 equal bins, the bin holding the 512th largest is kept and cut
+// again, until the keys at or above the kept bin number at most kCand.  Those
+// candidates (every key above the bin, every key in it) go to LDS as
+// (key << 32 | ~position) and a bitonic sort orders them: score descending,
+// then position ascending.  The first 512 are the selection.  Only a single key
+// value repeated more than kCand - 512 times at the threshold defeats the
+// bracketing; then an ordered pass over positions takes the keys above it and
+// the lowest positions holding it.
+constexpr int kCand = 4096;
 
 __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs a) {
   const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  const int npos = min(a.ctx_len[b], a.max_pages * kPage);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int npos = max(0, min(a.ctx_len[b], a.max_pages * kPage));
   const float* sc = a.scores + (int64_t)b * a.max_pages * kPage;
   __shared__ uint32_t hist[4096];
+  __shared__ uint32_t validw[kMaxPageWords];       // bit p: page p of this request is valid
+  __shared__ uint64_t cand[kCand];
+  __shared__ uint32_t red_lo[kSelThreads / 64], red_hi[kSelThreads / 64];
   __shared__ int wave_tot[kSelThreads / 64];
-  __shared__ uint64_t sel[kIdxTopk];
-  __shared__ uint32_t prefix_s, remaining_s;
-  __shared__ int cnt_s;
+  __shared__ uint32_t bin_s, above_s;
+  __shared__ int ncand_s;
 
-  // radix select of the kIdxTopk-th largest key among valid positions
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = kIdxTopk;
-  int nvalid = 0;
-  const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int sh = shifts[pass], nb = 1 << widths[pass];
-    for (int i = t; i < nb; i += kSelThreads) hist[i] = 0;
+  // page validity, from one coalesced pass over the request's page-table row
+  const int npages = (npos + kPage - 1) / kPage;
+  const bool bitmask = npages <= 32 * kMaxPageWords;
+  if (bitmask) {
+    for (int i = t; i < (npages + 31) / 32; i += kSelThreads) validw[i] = 0;
     __syncthreads();
-    int cnt = 0;
-    for (int s = t; s < npos; s += kSelThreads) {
-      int pg;
-      if (!page_ok(a, b, s, &pg)) continue;
-      const uint32_t k = order_key(sc[s]);
-      ++cnt;
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> sh) & (nb - 1)], 1u);
+    for (int p = t; p < npages; p += kSelThreads) {
+      const int pg = a.page_table[(int64_t)b * a.max_pages + p];
+      if (pg >= 0 && (int64_t)pg < a.pool_pages) atomicOr(&validw[p >> 5], 1u << (p & 31));
     }
-    __syncthreads();
-    if (pass == 0) {
-      // total valid positions (each thread's count, summed through LDS)
-      if (t == 0) cnt_s = 0;
-      __syncthreads();
-      atomicAdd(&cnt_s, cnt);
-      __syncthreads();
-      nvalid = cnt_s;
-      if (nvalid <= kIdxTopk) break;               // every valid position is selected
-    }
-    if (t == 0) {
-      // from the top bin down, find the one holding the remaining-th largest key
-      uint32_t above = 0;
-      int d = nb - 1;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= remaining) break;
-        above += hist[d];
-      }
-      prefix_s = prefix | ((uint32_t)d << sh);
-      remaining_s = remaining - above;
-    }
-    __syncthreads();
-    prefix = prefix_s;
-    remaining = remaining_s;
-    mask |= (uint32_t)(nb - 1) << sh;
-    __syncthreads();
   }
-  const bool all_valid = nvalid <= kIdxTopk;
-  const uint32_t T = prefix;                       // exact key of the kIdxTopk-th largest score
-
-  // collect, in position order: keys above T, and the first `remaining` keys equal to T
-  int taken_eq = 0, nsel = 0;
-  for (int base = 0; base < npos; base += kSelThreads) {
-    const int s = base + t;
-    int pg;
-    const bool v = s < npos && page_ok(a, b, s, &pg);
-    const uint32_t k = v ? order_key(sc[s]) : 0u;
-    const bool gt = v && (all_valid || k > T);
-    const bool eq = v && !all_valid && k == T;
-    int eq_tot;
-    const int eq_rank = taken_eq + block_scan(eq, wave_tot, &eq_tot);
-    const bool take = gt || (eq && eq_rank < (int)remaining);
-    int sel_tot;
-    const int slot = nsel + block_scan(take, wave_tot, &sel_tot);
-    if (take && slot < kIdxTopk) sel[slot] = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)s;
-    taken_eq += eq_tot;
-    nsel += sel_tot;
-  }
-  nsel = min(nsel, kIdxTopk);
-  for (int i = nsel + t; i < kIdxTopk; i += kSelThreads) sel[i] = 0ull;   // sorts last
+  if (t == 0) ncand_s = 0;
   __syncthreads();
-
-  // bitonic sort, descending: score descending, then position ascending
-  for (int size = 2; size <= kIdxTopk; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (t < kIdxTopk / 2) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool desc = (i & size) == 0;
-        const uint64_t x = sel[i], y = sel[j];
-        if ((x < y) == desc) {
-          sel[i] = y;
-          sel[j] = x;
+  // s0 is a multiple of 4: the four positions share one page
+  auto page_valid = [&](int s0) -> bool {
+    if (bitmask) return (validw[s0 >> 11] >> ((s0 >> 6) & 31)) & 1u;
+    int pg;
+    return page_ok(a, b, s0, &pg);
+  };
+  // visit every position in batches of 16 per thread (four 16-byte loads in
+  // flight); f(s, key, ok) is called by every lane, ok false for positions
+  // that are out of range or on an invalid page
+  auto for_positions = [&](auto&& f) {
+    for (int base = 0; base < npos; base += 16 * kSelThreads) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s0 = base + 4 * (t + u * kSelThreads);
+        if (s0 + 3 < npos) {
+          v[u] = *reinterpret_cast<const float4*>(sc + s0);
+        } else {
+          v[u].x = s0 < npos ? sc[s0] : 0.f;
+          v[u].y = s0 + 1 < npos ? sc[s0 + 1] : 0.f;
+          v[u].z = s0 + 2 < npos ? sc[s0 + 2] : 0.f;
+          v[u].w = 0.f;
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s0 = base + 4 * (t + u * kSelThreads);
+        const bool pv = s0 < npos && page_valid(s0);
+        const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f(s0 + i, order_key(vv[i]), pv && s0 + i < npos);
+      }
     }
+  };
+
+  // range and count of the valid keys
+  uint32_t klo = 0xffffffffu, khi = 0;
+  int cnt = 0;
+  for_positions([&](int, uint32_t k, bool ok) {
+    if (ok) {
+      klo = min(klo, k);
+      khi = max(khi, k);
+      ++cnt;
+    }
+  });
+  klo = wave_min(klo);
+  khi = wave_max(khi);
+  cnt = wave_sum(cnt);
+  if (lane == 0) {
+    red_lo[wave] = klo;
+    red_hi[wave] = khi;
+    wave_tot[wave] = cnt;
+  }
+  __syncthreads();
+  int nvalid = 0;
+  klo = 0xffffffffu;
+  khi = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    klo = min(klo, red_lo[w]);
+    khi = max(khi, red_hi[w]);
+    nvalid += wave_tot[w];
+  }
+  __syncthreads();
+
+  // bracket the threshold: keys in [lo, hi], `remaining` of them still to take
+  uint32_t lo = klo, hi = khi, remaining = kIdxTopk, incnt = (uint32_t)nvalid;
+  if (nvalid <= kIdxTopk) lo = 0;                  // every valid position is selected
+  while (nvalid > kIdxTopk && kIdxTopk - remaining + incnt > (uint32_t)kCand && hi > lo) {
+    const uint32_t range = hi - lo;
+    const int sh = range < 4096u ? 0 : (32 - __clz(range)) - 12;
+    for (int i = t; i < 4096; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for_positions([&](int, uint32_t k, bool ok) {
+      if (ok && k >= lo && k <= hi) atomicAdd(&hist[(k - lo) >> sh], 1u);
+    });
+    __syncthreads();
+    // thread t owns bins 4 (1023 - t) .. + 3; counts above its bins by a scan
+    const int r = kSelThreads - 1 - t;
+    const uint32_t h0 = hist[4 * r], h1 = hist[4 * r + 1], h2 = hist[4 * r + 2], h3 = hist[4 * r + 3];
+    int tot;
+    uint32_t acc = (uint32_t)block_scan((int)(h0 + h1 + h2 + h3), wave_tot, &tot);
+    const uint32_t hv[4] = {h0, h1, h2, h3};
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (acc < remaining && acc + hv[j] >= remaining) {
+        bin_s = 4 * r + j;
+        above_s = acc;
+      }
+      acc += hv[j];
+    }
+    __syncthreads();
+    const uint32_t d = bin_s;
+    remaining -= above_s;
+    incnt = hist[d];
+    lo = lo + (d << sh);
+    hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << sh) - 1));
+    __syncthreads();
+  }
+  const uint32_t nabove = kIdxTopk - remaining;   // valid keys above hi
+  int nsel;
+  if (nvalid <= kIdxTopk || nabove + incnt <= (uint32_t)kCand) {
+    // candidates: every valid key >= lo (at most kCand), appended wave by wave
+    for_positions([&](int s, uint32_t k, bool ok) {
+      const bool take = ok && k >= lo;
+      const uint64_t m = __ballot(take);
+      if (m) {
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&ncand_s, __popcll(m));
+        base = __shfl(base, leader, 64);
+        const int off = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (take && base + off < kCand) cand[base + off] = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)s;
+      }
+    });
+    __syncthreads();
+    const int n = min(ncand_s, kCand);
+    nsel = min(n, kIdxTopk);
+    int P = kIdxTopk;
+    while (P < n) P <<= 1;
+    for (int i = n + t; i < P; i += kSelThreads) cand[i] = 0ull;   // sorts last
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int q = t; q < P / 2; q += kSelThreads) {
+          const int i = 2 * q - (q & (stride - 1));
+          const int j = i + stride;
+          const bool desc = (i & size) == 0;
+          const uint64_t x = cand[i], y = cand[j];
+          if ((x < y) == desc) {
+            cand[i] = y;
+            cand[j] = x;
+          }
+        }
+        __syncthreads();
+      }
+  } else {
+    // one key T = lo = hi repeated too often: the keys above T, then the lowest
+    // `remaining` positions holding T.  Thread t walks positions
+    // [t L, (t + 1) L) twice: counting, then (after prefix sums over threads,
+    // i.e. over positions) writing.
+    const uint32_t T = lo;
+    const int L = (npos + kSelThreads - 1) / kSelThreads;
+    const int s_lo = min(npos, t * L), s_hi = min(npos, s_lo + L);
+    int ngt = 0, neq = 0;
+    for (int s = s_lo; s < s_hi; ++s) {
+      if (!page_valid(s & ~3)) continue;
+      const uint32_t k = order_key(sc[s]);
+      ngt += k > T ? 1 : 0;
+      neq += k == T ? 1 : 0;
+    }
+    int gt_tot, eq_tot;
+    int gt_at = block_scan(ngt, wave_tot, &gt_tot);
+    int eq_at = block_scan(neq, wave_tot, &eq_tot);
+    for (int s = s_lo; s < s_hi; ++s) {
+      if (!page_valid(s & ~3)) continue;
+      const uint32_t k = order_key(sc[s]);
+      const uint64_t e = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)s;
+      if (k > T) {
+        if (gt_at < kIdxTopk) cand[gt_at] = e;
+        ++gt_at;
+      } else if (k == T) {
+        if (eq_at < (int)remaining && gt_tot + eq_at < kIdxTopk) cand[gt_tot + eq_at] = e;
+        ++eq_at;
+      }
+    }
+    nsel = min(kIdxTopk, gt_tot + min(eq_tot, (int)remaining));
+    __syncthreads();
+    for (int i = nsel + t; i < kIdxTopk; i += kSelThreads) cand[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= kIdxTopk; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        if (t < kIdxTopk / 2) {
+          const int i = 2 * t - (t & (stride - 1));
+          const int j = i + stride;
+          const bool desc = (i & size) == 0;
+          const uint64_t x = cand[i], y = cand[j];
+          if ((x < y) == desc) {
+            cand[i] = y;
+            cand[j] = x;
+          }
+        }
+        __syncthreads();
+      }
+  }
   for (int j = t; j < kIdxTopk; j += kSelThreads)
-    a.topk[(int64_t)b * kIdxTopk + j] = j < nsel ? (int32_t)~(uint32_t)(sel[j] & 0xffffffffull) : -1;
+    a.topk[(int64_t)b * kIdxTopk + j] = j < nsel ? (int32_t)~(uint32_t)(cand[j] & 0xffffffffull) : -1;
 }
 
 }  // namespace
@@ -240,8 +479,8 @@ hipError_t launch_indexer(const IndexerArgs& a, int B, hipStream_t stream) {
   if (B <= 0) return hipSuccess;
   {
     const int64_t npos = (int64_t)a.max_pages * kPage;
-    const dim3 grid((unsigned)((npos + kIdxPosPerWg - 1) / kIdxPosPerWg), B);
-    hipLaunchKernelGGL(indexer_score_kernel, grid, dim3(64 * kIdxWaves), 0, stream, a);
+    const dim3 grid((unsigned)((npos + kScPosPerWg - 1) / kScPosPerWg), B);
+    hipLaunchKernelGGL(indexer_score_kernel, grid, dim3(64 * kScWaves), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

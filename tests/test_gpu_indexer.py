@@ -98,3 +98,22 @@ def test_indexer_feeds_decode():
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.decode_workload(w)
     assert_parity(out, lse, ref_o, ref_l, "decode over the indexer's selection")
+
+
+def test_indexer_heavy_ties():
+    """Ties at the threshold: the lowest positions win, whether the tied key
+    fits the kernel's candidate set or not."""
+    inp = W.indexer_inputs(3, [9000, 20000, 20000], 15)
+    inp.q[0] = 0                                        # request 0: 9000 equal scores
+    ref_sc, _ = oracle.indexer(inp.q, inp.w, inp.keys, inp.pool_pages, inp.page_table, inp.ctx_len)
+    slot = lambda b, s: int(inp.page_table[b, s // W.PAGE]) * W.PAGE + s % W.PAGE
+    for b, copies in ((1, 6000), (2, 1000)):           # the 301st best key copied onto low scorers
+        order = np.argsort(-ref_sc[b][:inp.ctx_len[b]], kind="stable")
+        src = int(order[300])
+        for s in order[-copies:]:
+            inp.keys[slot(b, int(s))] = inp.keys[slot(b, src)]
+    idx, sc = _check(inp, "indexer heavy ties")
+    assert list(idx[0]) == list(range(512))
+    for b in (1, 2):
+        t = sc[b][int(np.argsort(-ref_sc[b][:inp.ctx_len[b]], kind="stable")[300])]
+        assert (sc[b][idx[b]] >= t).all() and (sc[b][idx[b]] == t).sum() > 100
