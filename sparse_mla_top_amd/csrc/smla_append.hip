@@ -14,7 +14,7 @@
 // coalescing: one wave per token, every lane moving 8 consecutive latent values.
 #include <hip/hip_runtime.h>
 
-#include "smla_internal.h"
+#include "smla_cache_ops.h"
 
 namespace smla {
 

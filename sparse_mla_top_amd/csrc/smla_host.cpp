@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "../../include/sparse_mla.h"
+#include "smla_cache_ops.h"
 #include "smla_internal.h"
 
 using namespace smla;

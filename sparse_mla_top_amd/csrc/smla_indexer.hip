@@ -25,7 +25,7 @@
 
 #include <type_traits>
 
-#include "smla_internal.h"
+#include "smla_cache_ops.h"
 
 namespace smla {
 
@@ -41,6 +41,7 @@ constexpr int kScPosPerWave = kScPagesPerWave * kPage;
 constexpr int kScPosPerWg = kScPosPerWave * kScWaves;
 constexpr int kTileBytes = 16 * kIdxDim * 2;       // 16 key rows
 constexpr int kSelThreads = 1024;                  // select kernel
+constexpr int kSelVec = 4;                         // select: 16-byte score loads per thread per batch
 constexpr int kMaxPageWords = 4096;                // page-validity bitmask in LDS: up to 131072 pages
 static_assert(kScPagesPerWave <= 64, "page ids are held one per lane");
 
@@ -290,14 +291,14 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
     int pg;
     return page_ok(a, b, s0, &pg);
   };
-  // visit every position in batches of 16 per thread (four 16-byte loads in
-  // flight); f(s, key, ok) is called by every lane, ok false for positions
-  // that are out of range or on an invalid page
+  // visit every position in batches of 4 kSelVec per thread (kSelVec 16-byte
+  // loads per thread in flight); f(s, key, ok) is called by every lane, ok
+  // false for positions that are out of range or on an invalid page
   auto for_positions = [&](auto&& f) {
-    for (int base = 0; base < npos; base += 16 * kSelThreads) {
-      float4 v[4];
+    for (int base = 0; base < npos; base += 4 * kSelVec * kSelThreads) {
+      float4 v[kSelVec];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kSelVec; ++u) {
         const int s0 = base + 4 * (t + u * kSelThreads);
         if (s0 + 3 < npos) {
           v[u] = *reinterpret_cast<const float4*>(sc + s0);
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kSelVec; ++u) {
         const int s0 = base + 4 * (t + u * kSelThreads);
         const bool pv = s0 < npos && page_valid(s0);
         const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
