@@ -258,6 +258,9 @@ __device__ __forceinline__ int wave_sum(int v) {
 // bracketing; then an ordered pass over positions takes the keys above it and
 // the lowest positions holding it.
 constexpr int kCand = 4096;
+constexpr int kSampleMin = 32768;        // contexts from this many positions start from a sample
+constexpr int kSampleLines = 256;        // 128-byte lines sampled: 8192 keys
+constexpr int kSampleTarget = 1500;      // keys expected above the estimated bound
 
 __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs a) {
   const int b = blockIdx.x;
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
   if (t == 0) ncand_s = 0;
   __syncthreads();
   // s0 is a multiple of 4: the four positions share one page
-  auto page_valid = [&](int s0) -> bool {
+  auto page_valid = [&, npos](int s0) __attribute__((always_inline)) -> bool {
     if (bitmask) return (validw[s0 >> 11] >> ((s0 >> 6) & 31)) & 1u;
     int pg;
     return page_ok(a, b, s0, &pg);
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
   // visit every position in batches of 4 kSelVec per thread (kSelVec 16-byte
   // loads per thread in flight); f(s, key, ok) is called by every lane, ok
   // false for positions that are out of range or on an invalid page
-  auto for_positions = [&](auto&& f) {
+  auto for_positions = [&, npos](auto&& f) __attribute__((always_inline)) {
     for (int base = 0; base < npos; base += 4 * kSelVec * kSelThreads) {
       float4 v[kSelVec];
 #pragma unroll
@@ -320,57 +323,39 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
     }
   };
 
-  // range and count of the valid keys
-  uint32_t klo = 0xffffffffu, khi = 0;
-  int cnt = 0;
-  for_positions([&](int, uint32_t k, bool ok) {
-    if (ok) {
-      klo = min(klo, k);
-      khi = max(khi, k);
-      ++cnt;
+  // Block reductions: min and max of a key, sum of a count (all threads get them).
+  auto block_range = [&, npos](uint32_t& klo, uint32_t& khi, int& cnt) __attribute__((always_inline)) {
+    klo = wave_min(klo);
+    khi = wave_max(khi);
+    cnt = wave_sum(cnt);
+    if (lane == 0) {
+      red_lo[wave] = klo;
+      red_hi[wave] = khi;
+      wave_tot[wave] = cnt;
     }
-  });
-  klo = wave_min(klo);
-  khi = wave_max(khi);
-  cnt = wave_sum(cnt);
-  if (lane == 0) {
-    red_lo[wave] = klo;
-    red_hi[wave] = khi;
-    wave_tot[wave] = cnt;
-  }
-  __syncthreads();
-  int nvalid = 0;
-  klo = 0xffffffffu;
-  khi = 0;
+    __syncthreads();
+    klo = 0xffffffffu;
+    khi = 0;
+    cnt = 0;
 #pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
-    klo = min(klo, red_lo[w]);
-    khi = max(khi, red_hi[w]);
-    nvalid += wave_tot[w];
-  }
-  __syncthreads();
-
-  // bracket the threshold: keys in [lo, hi], `remaining` of them still to take
-  uint32_t lo = klo, hi = khi, remaining = kIdxTopk, incnt = (uint32_t)nvalid;
-  if (nvalid <= kIdxTopk) lo = 0;                  // every valid position is selected
-  while (nvalid > kIdxTopk && kIdxTopk - remaining + incnt > (uint32_t)kCand && hi > lo) {
-    const uint32_t range = hi - lo;
-    const int sh = range < 4096u ? 0 : (32 - __clz(range)) - 12;
-    for (int i = t; i < 4096; i += kSelThreads) hist[i] = 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      klo = min(klo, red_lo[w]);
+      khi = max(khi, red_hi[w]);
+      cnt += wave_tot[w];
+    }
     __syncthreads();
-    for_positions([&](int, uint32_t k, bool ok) {
-      if (ok && k >= lo && k <= hi) atomicAdd(&hist[(k - lo) >> sh], 1u);
-    });
-    __syncthreads();
-    // thread t owns bins 4 (1023 - t) .. + 3; counts above its bins by a scan
+  };
+  // Over hist[0..4096), the bin d holding the want-th largest entry (counting
+  // from the top bin down, want <= total); *above = entries in bins above d.
+  // Thread t owns bins 4 (1023 - t) .. + 3; a prefix scan counts the bins above.
+  auto crossing_bin = [&, npos](uint32_t want, uint32_t* above) __attribute__((always_inline)) -> uint32_t {
     const int r = kSelThreads - 1 - t;
-    const uint32_t h0 = hist[4 * r], h1 = hist[4 * r + 1], h2 = hist[4 * r + 2], h3 = hist[4 * r + 3];
+    const uint32_t hv[4] = {hist[4 * r], hist[4 * r + 1], hist[4 * r + 2], hist[4 * r + 3]};
     int tot;
-    uint32_t acc = (uint32_t)block_scan((int)(h0 + h1 + h2 + h3), wave_tot, &tot);
-    const uint32_t hv[4] = {h0, h1, h2, h3};
+    uint32_t acc = (uint32_t)block_scan((int)(hv[0] + hv[1] + hv[2] + hv[3]), wave_tot, &tot);
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
-      if (acc < remaining && acc + hv[j] >= remaining) {
+      if (acc < want && acc + hv[j] >= want) {
         bin_s = 4 * r + j;
         above_s = acc;
       }
@@ -378,17 +363,15 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
     }
     __syncthreads();
     const uint32_t d = bin_s;
-    remaining -= above_s;
-    incnt = hist[d];
-    lo = lo + (d << sh);
-    hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << sh) - 1));
+    *above = above_s;
     __syncthreads();
-  }
-  const uint32_t nabove = kIdxTopk - remaining;   // valid keys above hi
-  int nsel;
-  if (nvalid <= kIdxTopk || nabove + incnt <= (uint32_t)kCand) {
-    // candidates: every valid key >= lo (at most kCand), appended wave by wave
-    for_positions([&](int s, uint32_t k, bool ok) {
+    return d;
+  };
+  auto bin_shift = [](uint32_t range) __attribute__((always_inline)) { return range < 4096u ? 0 : (32 - __clz(range)) - 12; };
+  // Append every valid key >= lo to cand (wave by wave: ballot, one atomic);
+  // ncand_s counts them all, only the first kCand are stored.
+  auto collect = [&, npos](uint32_t lo) __attribute__((always_inline)) {
+    for_positions([&](int s, uint32_t k, bool ok) __attribute__((always_inline)) {
       const bool take = ok && k >= lo;
       const uint64_t m = __ballot(take);
       if (m) {
@@ -401,26 +384,166 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
       }
     });
     __syncthreads();
+  };
+
+  // Sort cand[0..P) descending (P a power of two, 512 .. kCand).  Thread t
+  // holds entries t + 1024 m; stages whose partner lies within 64 entries pair
+  // lanes of one wave and run in registers (lane shuffles, no barrier); the
+  // wider stages exchange through LDS with a barrier each.
+  auto sort_desc = [&, npos](int P) __attribute__((always_inline)) {
+    const int per = P > kSelThreads ? P / kSelThreads : 1;
+    const bool holds = t < P;                      // whole waves: P is a multiple of 64
+    uint64_t x[kCand / kSelThreads];
+    auto in_regs = [&](int size, int stride) __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < kCand / kSelThreads; ++m) {
+        if (m < per) {
+          const int i = t + kSelThreads * m;
+          const uint32_t lo32 = (uint32_t)__shfl_xor((int)(uint32_t)x[m], stride, 64);
+          const uint32_t hi32 = (uint32_t)__shfl_xor((int)(uint32_t)(x[m] >> 32), stride, 64);
+          const uint64_t y = ((uint64_t)hi32 << 32) | lo32;
+          const bool keep_max = ((i & stride) == 0) == ((i & size) == 0);
+          x[m] = keep_max ? (x[m] > y ? x[m] : y) : (x[m] < y ? x[m] : y);
+        }
+      }
+    };
+    auto load = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < kCand / kSelThreads; ++m)
+        if (m < per) x[m] = cand[t + kSelThreads * m];
+    };
+    auto store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < kCand / kSelThreads; ++m)
+        if (m < per) cand[t + kSelThreads * m] = x[m];
+    };
+    if (holds) {
+      load();
+      for (int size = 2; size <= 64; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) in_regs(size, stride);
+      store();
+    }
+    __syncthreads();
+    for (int size = 128; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride >= 64; stride >>= 1) {
+        for (int q = t; q < P / 2; q += kSelThreads) {
+          const int i = 2 * q - (q & (stride - 1));
+          const int j = i + stride;
+          const bool desc = (i & size) == 0;
+          const uint64_t a0 = cand[i], a1 = cand[j];
+          if ((a0 < a1) == desc) {
+            cand[i] = a1;
+            cand[j] = a0;
+          }
+        }
+        __syncthreads();
+      }
+      if (holds) {
+        load();
+        for (int stride = 32; stride > 0; stride >>= 1) in_regs(size, stride);
+        store();
+      }
+      __syncthreads();
+    }
+  };
+
+  // Estimate from a sample: kSampleLines evenly spaced 128-byte lines of scores
+  // (8 threads per line, 8 keys per thread).  A lower bound that about
+  // kSampleTarget valid keys clear is read off their histogram; one pass then
+  // collects every key above it.  With at least kIdxTopk and at most kCand
+  // candidates the selection is among them (every other key is smaller); else
+  // the exact path below runs.
+  bool cand_ok = false;
+  if (npos >= kSampleMin) {
+    const int nlines = npos / 32;
+    uint32_t sk[8];
+    uint32_t slo = 0xffffffffu, shi = 0;
+    int nsv = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int line = r * (kSelThreads / 8) + (t >> 3);
+      const int s0 = (int)((int64_t)line * nlines / kSampleLines) * 32 + 4 * (t & 7);   // s0 + 3 < npos
+      const float4 v = *reinterpret_cast<const float4*>(sc + s0);
+      const bool pv = page_valid(s0);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t k = order_key(vv[i]);
+        sk[4 * r + i] = pv ? k : 0u;
+        if (pv) {
+          slo = min(slo, k);
+          shi = max(shi, k);
+          ++nsv;
+        }
+      }
+    }
+    block_range(slo, shi, nsv);
+    const uint32_t want = (uint32_t)max(1, (int)((int64_t)kSampleTarget * 8 * kSelThreads / npos));
+    if ((uint32_t)nsv >= want) {
+      const int sh = bin_shift(shi - slo);
+      for (int i = t; i < 4096; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (sk[i] >= slo && sk[i] != 0u) atomicAdd(&hist[(sk[i] - slo) >> sh], 1u);
+      __syncthreads();
+      uint32_t above;
+      const uint32_t d = crossing_bin(want, &above);
+      collect(slo + (d << sh));
+      const int n = ncand_s;
+      cand_ok = n >= kIdxTopk && n <= kCand;
+      __syncthreads();
+      if (!cand_ok && t == 0) ncand_s = 0;
+      __syncthreads();
+    }
+  }
+
+  int nsel = 0;
+  uint32_t lo = 0, remaining = kIdxTopk;
+  if (!cand_ok) {
+    // exact path: range and count of the valid keys
+    uint32_t klo = 0xffffffffu, khi = 0;
+    int nvalid = 0;
+    for_positions([&](int, uint32_t k, bool ok) __attribute__((always_inline)) {
+      if (ok) {
+        klo = min(klo, k);
+        khi = max(khi, k);
+        ++nvalid;
+      }
+    });
+    block_range(klo, khi, nvalid);
+    // bracket the threshold: keys in [lo, hi], `remaining` of them still to take
+    uint32_t hi = khi, incnt = (uint32_t)nvalid;
+    lo = nvalid <= kIdxTopk ? 0 : klo;             // at most kIdxTopk: every valid position is selected
+    while (nvalid > kIdxTopk && kIdxTopk - remaining + incnt > (uint32_t)kCand && hi > lo) {
+      const int sh = bin_shift(hi - lo);
+      for (int i = t; i < 4096; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for_positions([&](int, uint32_t k, bool ok) __attribute__((always_inline)) {
+        if (ok && k >= lo && k <= hi) atomicAdd(&hist[(k - lo) >> sh], 1u);
+      });
+      __syncthreads();
+      uint32_t above;
+      const uint32_t d = crossing_bin(remaining, &above);
+      remaining -= above;
+      incnt = hist[d];
+      lo = lo + (d << sh);
+      hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + ((1ull << sh) - 1));
+      __syncthreads();
+    }
+    if (nvalid <= kIdxTopk || kIdxTopk - remaining + incnt <= (uint32_t)kCand) {
+      collect(lo);                                 // at most kCand keys
+      cand_ok = true;
+    }
+  }
+  if (cand_ok) {
     const int n = min(ncand_s, kCand);
     nsel = min(n, kIdxTopk);
     int P = kIdxTopk;
     while (P < n) P <<= 1;
     for (int i = n + t; i < P; i += kSelThreads) cand[i] = 0ull;   // sorts last
     __syncthreads();
-    for (int size = 2; size <= P; size <<= 1)
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int q = t; q < P / 2; q += kSelThreads) {
-          const int i = 2 * q - (q & (stride - 1));
-          const int j = i + stride;
-          const bool desc = (i & size) == 0;
-          const uint64_t x = cand[i], y = cand[j];
-          if ((x < y) == desc) {
-            cand[i] = y;
-            cand[j] = x;
-          }
-        }
-        __syncthreads();
-      }
+    sort_desc(P);
   } else {
     // one key T = lo = hi repeated too often: the keys above T, then the lowest
     // `remaining` positions holding T.  Thread t walks positions
@@ -455,20 +578,7 @@ __global__ __launch_bounds__(kSelThreads) void indexer_select_kernel(IndexerArgs
     __syncthreads();
     for (int i = nsel + t; i < kIdxTopk; i += kSelThreads) cand[i] = 0ull;
     __syncthreads();
-    for (int size = 2; size <= kIdxTopk; size <<= 1)
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        if (t < kIdxTopk / 2) {
-          const int i = 2 * t - (t & (stride - 1));
-          const int j = i + stride;
-          const bool desc = (i & size) == 0;
-          const uint64_t x = cand[i], y = cand[j];
-          if ((x < y) == desc) {
-            cand[i] = y;
-            cand[j] = x;
-          }
-        }
-        __syncthreads();
-      }
+    sort_desc(kIdxTopk);
   }
   for (int j = t; j < kIdxTopk; j += kSelThreads)
     a.topk[(int64_t)b * kIdxTopk + j] = j < nsel ? (int32_t)~(uint32_t)(cand[j] & 0xffffffffull) : -1;

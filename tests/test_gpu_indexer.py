@@ -117,3 +117,22 @@ def test_indexer_heavy_ties():
     for b in (1, 2):
         t = sc[b][int(np.argsort(-ref_sc[b][:inp.ctx_len[b]], kind="stable")[300])]
         assert (sc[b][idx[b]] >= t).all() and (sc[b][idx[b]] == t).sum() > 100
+
+
+def test_indexer_long_context_fallbacks():
+    """Long contexts where an estimate from a sample of the scores cannot stand:
+    every score equal (far too many candidates, then ties by position), almost
+    every page invalid (too few valid keys), and invalid pages scattered."""
+    inp = W.indexer_inputs(3, [65536, 65536, 40000], 16)
+    inp.q[0] = 0
+    keep = [3, 200, 511, 700, 1023]
+    for p in range(inp.page_table.shape[1]):
+        if p not in keep:
+            inp.page_table[1, p] = -1
+    for p in range(0, 625, 37):
+        inp.page_table[2, p] = inp.pool_pages + p
+    idx, _ = _check(inp, "indexer long-context fallbacks")
+    assert list(idx[0]) == list(range(512))
+    got = sorted(int(s) for s in idx[1] if s >= 0)
+    assert got == sorted(p * W.PAGE + i for p in keep for i in range(W.PAGE)) and np.all(idx[1][320:] == -1)
+    assert not np.any(np.isin(idx[2] // W.PAGE, list(range(0, 625, 37))))
