@@ -93,7 +93,8 @@ typedef struct {
 #define SMLA_MERGE_AUTO 0      /* in a plan passed in: let the selector choose; in a plan
                                   returned: nothing to merge (nsplit = 1)                  */
 #define SMLA_MERGE_IN_KERNEL 1 /* the last split of each request to finish merges them, in
-                                  the same launch                                          */
+                                  the same launch; only for batch * q_len <= 4096 (a plan
+                                  forcing it beyond that returns SMLA_ERR_PLAN)            */
 #define SMLA_MERGE_SEPARATE 2  /* a second launch: the combine kernel                      */
 
 /* Launch plan.  Zero fields mean "choose automatically". */
@@ -147,10 +148,13 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *   shape      [host]   problem description
  *   plan_or_null [host] NULL = automatic plan; else as for smla_plan_for's override
  *   workspace  [device] scratch of at least the size smla_plan_for reports
- *                        (may be NULL when that size is 0).  It holds the split
- *                        partials and arrival counters per query token: it must be
- *                        zero-filled once before its first use (smla_workspace_init),
- *                        and every successful call leaves the counters at zero again.
+ *                        (may be NULL when that size is 0).  Its first 64 KiB hold
+ *                        the arrival counters of the in-kernel merge, at the same
+ *                        place for every shape and plan; the split partials follow.
+ *                        It must be zero-filled once before its first use
+ *                        (smla_workspace_init); every successful call leaves the
+ *                        counters at zero again, so one workspace serves calls of
+ *                        any batch size and split count that fit in it.
  *                        Calls that share a workspace must not overlap in time.
  *   stream     hipStream_t (NULL = default stream)
  * With nsplit = 1 the work is one kernel launch.  Otherwise each (request,

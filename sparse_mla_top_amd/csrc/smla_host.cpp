@@ -58,14 +58,21 @@ int query_sets(const smla_shape* s) { return s->batch * q_len_of(s); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout (nsplit > 1), per query set (request, query token), Q sets
-// in all: fp32 partial outputs [Q, nsplit, 64, 512], fp32 partial lse
-// [Q, nsplit, 64], uint32 counters [Q][head group][2] (arrival tickets,
-// finished partial writes); each region starts at a 256-byte boundary.
+// in all: a fixed 64 KiB head of uint32 arrival counters [Q][head group][2]
+// (tickets, finished partial writes; room for kMaxMergeSets sets), then fp32
+// partial outputs [Q, nsplit, 64, 512] and fp32 partial lse [Q, nsplit, 64],
+// each region at a 256-byte boundary.  The counters sit at the same place for
+// every shape and plan, and partial writes never reach them, so a workspace
+// reused across batch sizes and split counts finds them at zero (each call
+// that merges in-kernel resets its own).
+constexpr int kMaxMergeSets = 4096;
+constexpr size_t kCounterBytes = (size_t)kMaxMergeSets * kHeadGroups * 2 * sizeof(uint32_t);
+static_assert(kCounterBytes % 256 == 0, "counter head keeps the partials 256-byte aligned");
 size_t ws_part_o_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * kDv * sizeof(float)); }
 size_t ws_part_lse_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * sizeof(float)); }
 size_t workspace_for(int B, int nsplit) {
   if (nsplit <= 1 || B == 0) return 0;
-  return ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit) + align256((size_t)B * kHeadGroups * 2 * sizeof(uint32_t));
+  return kCounterBytes + ws_part_o_bytes(B, nsplit) + ws_part_lse_bytes(B, nsplit);
 }
 
 // Estimated time (us) of one call with `nsplit` splits on `cus` compute units
@@ -161,10 +168,12 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
     if (forced != 0 && ns != forced) continue;
     for (int m = SMLA_MERGE_IN_KERNEL; m <= SMLA_MERGE_SEPARATE; ++m) {
       if (p.merge != SMLA_MERGE_AUTO && m != p.merge) continue;
+      if (m == SMLA_MERGE_IN_KERNEL && ns > 1 && query_sets(shape) > kMaxMergeSets) continue;
       const double t = est_time_us(B > 0 ? B : 1, q_len_of(shape), ns, chunk, slots, m, smla_row_bytes(shape->kv_format));
       if (t < best - 1e-9) { best = t; best_ns = ns; best_merge = m; }
     }
   }
+  if (!std::isfinite(best)) return SMLA_ERR_PLAN;   // in-kernel merge forced beyond kMaxMergeSets
   p.nsplit = best_ns;
   p.merge = p.nsplit > 1 ? best_merge : SMLA_MERGE_AUTO;
   *out = p;
@@ -227,9 +236,9 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   a.part_lse = nullptr;
   a.counters = nullptr;
   if (plan.nsplit > 1) {
-    a.part_o = (float*)workspace;
-    a.part_lse = (float*)((uint8_t*)workspace + ws_part_o_bytes(Q, plan.nsplit));
-    a.counters = (uint32_t*)((uint8_t*)workspace + ws_part_o_bytes(Q, plan.nsplit) + ws_part_lse_bytes(Q, plan.nsplit));
+    a.counters = (uint32_t*)workspace;
+    a.part_o = (float*)((uint8_t*)workspace + kCounterBytes);
+    a.part_lse = (float*)((uint8_t*)workspace + kCounterBytes + ws_part_o_bytes(Q, plan.nsplit));
   }
   CombineArgs& c = pr->combine;
   c.part_o = a.part_o;
@@ -290,8 +299,8 @@ int smla_decode_combine(const smla_shape* shape, const smla_plan* plan_or_null, 
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15)) return SMLA_ERR_WORKSPACE;
   if ((uintptr_t)out & 7) return SMLA_ERR_INVALID_ARG;
   CombineArgs c;
-  c.part_o = (const float*)workspace;
-  c.part_lse = (const float*)((const uint8_t*)workspace + ws_part_o_bytes(query_sets(shape), plan.nsplit));
+  c.part_o = (const float*)((const uint8_t*)workspace + kCounterBytes);
+  c.part_lse = (const float*)((const uint8_t*)workspace + kCounterBytes + ws_part_o_bytes(query_sets(shape), plan.nsplit));
   c.nsplit = plan.nsplit;
   c.out = (uint16_t*)out;
   c.lse = lse;

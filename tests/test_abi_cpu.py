@@ -89,8 +89,8 @@ def test_forced_nsplit_normalised_to_whole_tiles(forced, expect):
     chunk = math.ceil(16 / p.nsplit)
     assert (p.nsplit - 1) * chunk < 16 <= p.nsplit * chunk
     a256 = lambda x: (x + 255) // 256 * 256
-    # partial outputs, partial lse, two counters (tickets, finished writes) per request and head group
-    assert ws == (0 if expect == 1 else a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4) + a256(8 * 16))
+    # a fixed 64 KiB head of arrival counters, then partial outputs and partial lse
+    assert ws == (0 if expect == 1 else 65536 + a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4))
 
 
 def test_selector_is_shape_only_and_bounded():
@@ -167,7 +167,7 @@ def test_query_tokens_scale_the_workspace_and_grid():
         a256 = lambda x: (x + 255) // 256 * 256
         for q in (1, 2, 3, 4):
             Q = 6 * q
-            assert ws[q] == a256(Q * ns * 64 * 512 * 4) + a256(Q * ns * 64 * 4) + a256(Q * 2 * 2 * 4)
+            assert ws[q] == 65536 + a256(Q * ns * 64 * 512 * 4) + a256(Q * ns * 64 * 4)
     # more query tokens never ask for more splits (the grid already fills more of the device)
     for B in (1, 4, 16, 32):
         picks = [smla.plan_for_cus(_shape(batch=B, q_len=q), 256)[0].nsplit for q in (1, 2, 3, 4)]
@@ -184,3 +184,16 @@ def test_kv_append_validation():
     assert L.smla_kv_append(ctypes.c_void_p(20), p, p, p, p, p, 4, ctypes.byref(s), None) == smla.ERR_INVALID_ARG
     assert L.smla_kv_append(p, p, p, p, p, p, 4, ctypes.byref(_shape(num_heads=8)), None) == smla.ERR_UNSUPPORTED_SHAPE
     assert L.smla_kv_append(p, p, p, p, p, p, 4, None, None) == smla.ERR_INVALID_ARG
+
+
+def test_in_kernel_merge_limited_to_counter_head():
+    """The arrival counters live in a fixed 64 KiB head (4096 query sets x two
+    head groups x two counters), so the in-kernel merge is never chosen beyond
+    4096 query sets and forcing it there is a plan error."""
+    p, ws = smla.plan_for_cus(_shape(batch=4096), 256, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL})
+    assert (p.nsplit, p.merge) == (2, smla.MERGE_IN_KERNEL)
+    for B, q in ((4097, 1), (1025, 4)):
+        p, _ = smla.plan_for_cus(_shape(batch=B, q_len=q), 256, {"nsplit": 2})
+        assert p.merge == smla.MERGE_SEPARATE
+        with pytest.raises(smla.SmlaError):
+            smla.plan_for_cus(_shape(batch=B, q_len=q), 256, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL})
