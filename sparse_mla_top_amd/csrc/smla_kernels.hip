@@ -76,7 +76,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       "s_mov_b32 m0, %1\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(lds_base)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))   // wave-uniform
       : "m0");
 }
 
@@ -918,6 +918,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
       }
+      // V^T of tile k first, so the reads' latency runs under the load issue
+      // below rather than ahead of the next barrier.
+      if (k < ntiles) read_v(k);
       // Tile k + kAhead goes out after this iteration's MFMAs: each 1 KB
       // direct-to-LDS instruction is slow to leave the issue queue, and the
       // MFMAs run meanwhile.  Its buffer held tile k - 2, done with by every
@@ -929,7 +932,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         issue(k + kAhead, nsrc);
         if (k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
       }
-      if (k < ntiles) read_v(k);
     }
 
     lds_barrier();                    // QK waves have published each half's max and sum
