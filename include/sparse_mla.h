@@ -42,6 +42,13 @@
  *     No C++ exception crosses this interface.
  *   - The library keeps no per-call state; concurrent calls on different
  *     streams are safe when their output and workspace buffers are disjoint.
+ *   - Out-of-range top-k indices and page ids are not errors: their slots are
+ *     masked.  Validate mode (environment SMLA_VALIDATE=1, read at every call)
+ *     is for tests and debugging.  sparse_mla_decode, smla_decode_split and
+ *     smla_gather_rows then first run a check kernel and wait for it on
+ *     `stream`.  They return SMLA_ERR_INDEX, launching nothing else, when an
+ *     entry other than -1 would be masked.  Calls in validate mode share one
+ *     device flag: they must not overlap, and cannot be graph-captured.
  */
 #ifndef SPARSE_MLA_H
 #define SPARSE_MLA_H
@@ -75,6 +82,9 @@ typedef enum {
 #define SMLA_ERR_WORKSPACE (-3)         /* workspace NULL or smaller than smla_plan_for says */
 #define SMLA_ERR_PLAN (-4)              /* an override plan outside the supported values    */
 #define SMLA_ERR_HIP (-5)               /* a HIP runtime call failed                        */
+#define SMLA_ERR_INDEX (-6)             /* validate mode only: a top-k index other than -1  */
+                                        /* outside [0, ctx_len), past the page-table row,   */
+                                        /* or on a page id outside [0, pool_pages)          */
 
 typedef struct {
     int32_t batch;             /* B >= 0 requests                                   */

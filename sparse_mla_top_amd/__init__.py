@@ -30,6 +30,7 @@ ERR_UNSUPPORTED_SHAPE = -2
 ERR_WORKSPACE = -3
 ERR_PLAN = -4
 ERR_HIP = -5
+ERR_INDEX = -6       # validate mode (environment SMLA_VALIDATE=1): an index or page id out of range
 
 MERGE_AUTO = 0
 MERGE_IN_KERNEL = 1

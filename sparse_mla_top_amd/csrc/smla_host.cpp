@@ -7,9 +7,12 @@
 #include <cstdint>
 #include <cstring>
 
+#include <cstdlib>
+
 #include "../../include/sparse_mla.h"
 #include "smla_cache_ops.h"
 #include "smla_internal.h"
+#include "smla_validate.h"
 
 using namespace smla;
 
@@ -132,6 +135,7 @@ const char* smla_strerror(int code) {
     case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
     case SMLA_ERR_PLAN: return "plan override outside the supported values";
     case SMLA_ERR_HIP: return "HIP runtime error";
+    case SMLA_ERR_INDEX: return "a top-k index or page id outside its range (validate mode)";
     default: return "unknown error";
   }
 }
@@ -188,6 +192,22 @@ int smla_plan_for(const smla_shape* shape, const smla_plan* ov, smla_plan* out, 
   rc = device_cus(&cus);
   if (rc) return rc;
   return smla_plan_for_cus(shape, ov, cus, out, workspace_bytes);
+}
+
+// Validate mode (environment SMLA_VALIDATE=1, read at every call): before any
+// launch, check the top-k indices and page ids and fail with SMLA_ERR_INDEX
+// where the kernels would mask a slot for a reason other than a -1 entry.
+// It adds a check kernel and a wait on the stream, so it is for tests and
+// debugging, not for graph capture.
+static int check_indices(const int32_t* page_table, const int32_t* topk_idx, const int32_t* ctx_len,
+                         const smla_shape* shape, void* stream) {
+  const char* v = std::getenv("SMLA_VALIDATE");
+  if (!v || v[0] != '1' || shape->batch == 0) return SMLA_OK;
+  unsigned bad = 0;
+  if (launch_validate(page_table, topk_idx, ctx_len, shape->batch, shape->max_pages_per_req, shape->pool_pages,
+                      (hipStream_t)stream, &bad) != hipSuccess)
+    return SMLA_ERR_HIP;
+  return bad ? SMLA_ERR_INDEX : SMLA_OK;
 }
 
 // Validated launch description shared by the decode entry points.
@@ -262,6 +282,8 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
   int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
+  rc = check_indices(page_table, topk_idx, ctx_len, shape, stream);
+  if (rc) return rc;
   if (pr.nsplit > 1 && pr.merge == SMLA_MERGE_SEPARATE) {
     pr.split.counters = nullptr;       // partials only; the combine launch merges them
     if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
@@ -281,6 +303,8 @@ int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_ta
   int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
                    workspace, workspace_bytes, &pr);
   if (rc || pr.B == 0) return rc;
+  rc = check_indices(page_table, topk_idx, ctx_len, shape, stream);
+  if (rc) return rc;
   pr.split.counters = nullptr;          // partials only; smla_decode_combine merges them
   if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
@@ -369,6 +393,8 @@ int smla_gather_rows(const void* kv_pool, const int32_t* page_table, const int32
   if (!kv_pool || !page_table || !topk_idx || !ctx_len || !rows || !slots) return SMLA_ERR_INVALID_ARG;
   if (((uintptr_t)kv_pool & 15) || ((uintptr_t)rows & 15)) return SMLA_ERR_INVALID_ARG;
   if (shape->batch == 0) return SMLA_OK;
+  rc = check_indices(page_table, topk_idx, ctx_len, shape, stream);
+  if (rc) return rc;
   GatherArgs g;
   g.pool = (const uint8_t*)kv_pool;
   g.page_table = page_table;

@@ -35,8 +35,14 @@ def test_version_and_row_bytes():
     assert L.smla_row_bytes(smla.KV_BF16) == 1152
     assert L.smla_row_bytes(smla.KV_FP8) == 656
     assert L.smla_row_bytes(7) == -1
-    for code in (0, -1, -2, -3, -4, -5, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
         assert smla.strerror(code)
+    # every error code has its own message, and the binding's constants are the header's
+    assert len({smla.strerror(c) for c in (-1, -2, -3, -4, -5, -6)}) == 6
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "sparse_mla.h")).read()
+    for name in ("INVALID_ARG", "UNSUPPORTED_SHAPE", "WORKSPACE", "PLAN", "HIP", "INDEX"):
+        m = re.search(r"#define SMLA_ERR_%s \((-\d+)\)" % name, hdr)
+        assert m and int(m.group(1)) == getattr(smla, "ERR_" + name), name
 
 
 def _shape(**kw):

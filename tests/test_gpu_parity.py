@@ -143,6 +143,56 @@ def test_invalid_page_ids_are_masked():
     _check(w, plan=2, what="invalid page ids")
 
 
+def test_validate_mode(monkeypatch):
+    """SMLA_VALIDATE=1: inputs the kernels would silently mask (an index other
+    than -1 outside [0, ctx_len), a page id outside the pool) are reported as
+    SMLA_ERR_INDEX before any launch, outputs untouched; -1 padding and valid
+    inputs pass and give the same bits as without the check."""
+    monkeypatch.setenv("SMLA_VALIDATE", "1")
+    w = W.build("validate", 944, 0, 3, [3000, 300, 5000], W.FMT_FP8, "uniform")   # request 1: -1 padding
+    d = upload(w)
+    shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages)
+    ok_out, ok_lse = _run(d, plan=2)
+    monkeypatch.delenv("SMLA_VALIDATE")
+    ref_out, ref_lse = _run(d, plan=2)
+    assert torch.equal(ok_out, ref_out) and torch.equal(ok_lse, ref_lse)
+    monkeypatch.setenv("SMLA_VALIDATE", "1")
+    smla.gather_rows(d.pool, d.page_table, d.topk_idx, d.ctx_len, kv_format=d.kv_format, pool_pages=d.pool_pages)
+    idx0, pt0 = w.topk_idx.copy(), w.page_table.copy()
+    bad_cases = []
+    for what, edit in (("index -2", lambda i, p: i.__setitem__((0, 7), -2)),
+                       ("index = ctx_len", lambda i, p: i.__setitem__((2, 100), w.ctx_len[2])),
+                       ("page id = pool_pages", lambda i, p: p.__setitem__((0, int(i[0, 3]) // W.PAGE), w.pool_pages)),
+                       ("page id -1", lambda i, p: p.__setitem__((2, int(i[2, 0]) // W.PAGE), -1))):
+        i, p = idx0.copy(), pt0.copy()
+        edit(i, p)
+        bad_cases.append((what, i, p))
+    for what, i, p in bad_cases:
+        _say(f"validate mode: {what}")
+        topk = torch.from_numpy(i).cuda()
+        pt = torch.from_numpy(p).cuda()
+        out = torch.full((w.B, 64, 512), 7, dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((w.B, 64), 7, dtype=torch.float32, device="cuda")
+        for plan in (1, 2):
+            ws = smla.new_workspace(smla.plan_for(shape, plan)[1] + 256)
+            rc = smla.decode_raw(d.q, d.pool, pt, topk, d.ctx_len, d.scale, out, lse, shape, plan, ws)
+            assert rc == smla.ERR_INDEX, (what, plan, rc)
+        with pytest.raises(smla.SmlaError):
+            smla.gather_rows(d.pool, pt, topk, d.ctx_len, kv_format=d.kv_format, pool_pages=d.pool_pages)
+        torch.cuda.synchronize()
+        assert torch.all(out == 7) and torch.all(lse == 7), what      # nothing launched
+        monkeypatch.delenv("SMLA_VALIDATE")                            # without the check: masked, no error
+        _run(upload_inputs(d, topk, pt), plan=2)
+        monkeypatch.setenv("SMLA_VALIDATE", "1")
+
+
+def upload_inputs(d, topk, pt):
+    import copy
+    e = copy.copy(d)
+    e.topk_idx, e.page_table = topk, pt
+    return e
+
+
 def test_permutation_invariance_on_gpu():
     w = W.make(2)
     d = upload(w)
