@@ -94,6 +94,9 @@ def main() -> int:
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer pass")
     ap.add_argument("--no-indexer", action="store_true", help="skip the top-k indexer pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--selector-sweep", action="store_true",
+                    help="time every split count and merge placement at B = 1..80 on the headline input sets "
+                         "and compare the selector's pick with the measured best")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -186,6 +189,45 @@ def main() -> int:
         else:
             traffic = t.get("hbm_bytes_per_launch")
             traffic_note = t.get("note", "")
+
+    # ------------------------------------------------------------------ selector check
+    # Every split count with no empty split and both merge placements, timed at
+    # B = 1 .. 80 on the first B requests of the same cold input sets; the
+    # selector's pick is compared with the measured best.
+    selector = None
+    if args.selector_sweep:
+        t4 = time.time()
+        selector = {}
+        for Bs in [b for b in SWEEP_B if b <= B]:
+            shp = smla.make_shape(Bs, w0.kv_format, w0.max_pages, pool_pages)
+            o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
+            l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
+            subs = [(d.q[:Bs], d.page_table[:Bs], d.topk_idx[:Bs], d.ctx_len[:Bs], d.scale) for _, d in sets]
+
+            def time_plan(pl):
+                p_, wsb = smla.plan_for(shp, pl)
+                w_s = smla.new_workspace(wsb, dev)
+
+                def scall(k):
+                    q_, pt_, ti_, cl_, sc_ = subs[k % L]
+                    rc = smla.decode_raw(q_, pool, pt_, ti_, cl_, sc_, o, l_, shp, pl, w_s, stream=stream)
+                    if rc != 0:
+                        raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
+                for k in range(10):
+                    scall(k)
+                return p_, statistics.median(timed(scall, args.sweep_steps) for _ in range(3))
+            pick, pick_us = time_plan(None)
+            table = {}
+            for ns in (1, 2, 3, 4, 6, 8, 16):
+                for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
+                    p_, us = time_plan({"nsplit": ns, "merge": merge})
+                    table[f"{p_.nsplit}/{'in-kernel' if merge == smla.MERGE_IN_KERNEL else 'separate' if merge else '-'}"] = round(us, 2)
+            best = min(table, key=table.get)
+            selector[str(Bs)] = {"pick": f"{pick.nsplit}/{'in-kernel' if pick.merge == smla.MERGE_IN_KERNEL else 'separate' if pick.merge else '-'}",
+                                 "pick_us": round(pick_us, 2), "best": best, "best_us": table[best],
+                                 "pick_over_best": round(pick_us / table[best], 3), "all_us": table}
+        log(f"selector sweep done in {time.time() - t4:.1f}s: "
+            f"{ {b: (v['pick'], v['best'], v['pick_over_best']) for b, v in selector.items()} }")
 
     # ------------------------------------------------------------------ query tokens
     # q_len query tokens per request sharing its selection, on the same cold
@@ -401,6 +443,7 @@ def main() -> int:
             "traffic_note": traffic_note,
             "sweep": sweep,
             "indexer_topk": indexer,
+            "selector_check": selector,
             "kv_append": None if append is None else {
                 "kernel": "append_kernel<1>", "format": "fp8 rows from fp32 latent/rope", "requests": 80,
                 "per_n_tokens": append},
