@@ -216,16 +216,19 @@ def main() -> int:
                 for k in range(10):
                     scall(k)
                 return p_, statistics.median(timed(scall, args.sweep_steps) for _ in range(3))
+            def label(p_):   # split count / merge placement of a plan as returned
+                where = {smla.MERGE_IN_KERNEL: "in-kernel", smla.MERGE_SEPARATE: "separate"}.get(p_.merge, "-")
+                return f"{p_.nsplit}/{where}"
             pick, pick_us = time_plan(None)
             table = {}
             for ns in (1, 2, 3, 4, 6, 8, 16):
                 for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
                     p_, us = time_plan({"nsplit": ns, "merge": merge})
-                    table[f"{p_.nsplit}/{'in-kernel' if merge == smla.MERGE_IN_KERNEL else 'separate' if merge else '-'}"] = round(us, 2)
+                    table[label(p_)] = round(us, 2)
             best = min(table, key=table.get)
-            selector[str(Bs)] = {"pick": f"{pick.nsplit}/{'in-kernel' if pick.merge == smla.MERGE_IN_KERNEL else 'separate' if pick.merge else '-'}",
-                                 "pick_us": round(pick_us, 2), "best": best, "best_us": table[best],
-                                 "pick_over_best": round(pick_us / table[best], 3), "all_us": table}
+            selector[str(Bs)] = {"pick": label(pick), "pick_us": round(pick_us, 2), "best": best,
+                                 "best_us": table[best], "pick_over_best": round(pick_us / table[best], 3),
+                                 "all_us": table}
         log(f"selector sweep done in {time.time() - t4:.1f}s: "
             f"{ {b: (v['pick'], v['best'], v['pick_over_best']) for b, v in selector.items()} }")
 
