@@ -350,3 +350,27 @@ def test_query_tokens_masked_and_degenerate():
     w = W.with_query_tokens(base, 2)
     for ns in (1, 4, 16):
         _check(w, plan=ns, what=f"q_len=2 degenerate nsplit={ns}")
+
+
+# --------------------------------------------------------------- large batches
+def test_large_batch_several_dispatch_rounds():
+    """600 requests: 1200 workgroups unsplit (several dispatch rounds on 256
+    CUs) and 2400 with two splits merged in-kernel (600 sets of counters)."""
+    w = W.build("large", 953, 0, 600, [600 + 37 * (b % 50) for b in range(600)], W.FMT_FP8, "uniform")
+    for plan in (None, {"nsplit": 1}, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL}):
+        _check(w, plan=plan, what=f"B=600 plan={plan}")
+
+
+def test_query_sets_beyond_the_in_kernel_merge_limit():
+    """1030 requests x 4 query tokens = 4120 query sets, past the 4096 the
+    arrival-counter head holds: a split plan merges with the combine launch,
+    and forcing the in-kernel merge is refused."""
+    base = W.build("qsets", 954, 0, 1030, [520] * 1030, W.FMT_FP8, "uniform")
+    w = W.with_query_tokens(base, 4)
+    d = upload(w)
+    shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages, 4)
+    p, _ = smla.plan_for(shape, {"nsplit": 2})
+    assert p.merge == smla.MERGE_SEPARATE
+    with pytest.raises(smla.SmlaError):
+        smla.plan_for(shape, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL})
+    _check(w, plan={"nsplit": 2}, what="4120 query sets, nsplit 2")
