@@ -116,14 +116,26 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
 
-    if args.copy_calibration:
-        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 x 1 GiB device copies done")
-        del x, y
+    # A plain 1 GiB device-to-device copy: its read + write rate is the HBM
+    # bandwidth a streaming kernel reaches on this device, reported beside the
+    # vendor peak.  (With --copy-calibration, run under rocprofv3's byte
+    # counters, the same copies scale FETCH_SIZE and WRITE_SIZE.)
+    x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    copy_ms = []
+    for _ in range(5):
+        ce0.record(stream)
+        y.copy_(x)
+        ce1.record(stream)
+        ce1.synchronize()
+        copy_ms.append(ce0.elapsed_time(ce1))
+    copy_gbs = 2 * x.numel() / (statistics.median(copy_ms) * 1e-3) / 1e9
+    log(f"device copy: {copy_gbs:.0f} GB/s read + write")
+    del x, y
 
     # ------------------------------------------------------------------ headline
     L = args.sets
@@ -333,6 +345,7 @@ def main() -> int:
                    "heads": 64, "head_dim": 128, "key_format": "bf16", "us": round(us, 2),
                    "algorithmic_bytes": int(byts), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                    "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "frac_of_device_copy": round(byts / (us * 1e-6) / 1e9 / copy_gbs, 4),
                    "mfma_frac_bf16_peak": round(flops / (us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4)}
         del keys, ipt, qi, wi, isc, iidx
         torch.cuda.empty_cache()
@@ -456,7 +469,8 @@ def main() -> int:
         },
         "roofline": {"kernel": KERNEL_NAME, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "device_copy_GBps": round(copy_gbs, 1),
+                     "frac_of_device_copy": round(achieved / copy_gbs, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
