@@ -5,9 +5,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstring>
-
 #include <cstdlib>
+#include <cstring>
 
 #include "../../include/sparse_mla.h"
 #include "smla_cache_ops.h"

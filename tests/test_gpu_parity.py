@@ -1,6 +1,8 @@
 """HIP path vs the fp64 oracle, through the C ABI (needs an MI355X)."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -182,15 +184,8 @@ def test_validate_mode(monkeypatch):
         torch.cuda.synchronize()
         assert torch.all(out == 7) and torch.all(lse == 7), what      # nothing launched
         monkeypatch.delenv("SMLA_VALIDATE")                            # without the check: masked, no error
-        _run(upload_inputs(d, topk, pt), plan=2)
+        _run(dataclasses.replace(d, topk_idx=topk, page_table=pt), plan=2)
         monkeypatch.setenv("SMLA_VALIDATE", "1")
-
-
-def upload_inputs(d, topk, pt):
-    import copy
-    e = copy.copy(d)
-    e.topk_idx, e.page_table = topk, pt
-    return e
 
 
 def test_permutation_invariance_on_gpu():
