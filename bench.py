@@ -94,6 +94,8 @@ def main() -> int:
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer pass")
     ap.add_argument("--no-indexer", action="store_true", help="skip the top-k indexer pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other standard workloads (B=1 bf16, B=32, B=96 ragged)")
     ap.add_argument("--selector-sweep", action="store_true",
                     help="time every split count and merge placement at B = 1..80 on the headline input sets "
                          "and compare the selector's pick with the measured best")
@@ -243,6 +245,46 @@ def main() -> int:
                                  "all_us": table}
         log(f"selector sweep done in {time.time() - t4:.1f}s: "
             f"{ {b: (v['pick'], v['best'], v['pick_over_best']) for b, v in selector.items()} }")
+
+    # ------------------------------------------------------------------ the other standard workloads
+    # B=1 with bf16 rows (4096-token context), B=32 (65536), B=96 ragged
+    # (log-uniform contexts from 128 to 524288, -1 padding): 8 cold input sets
+    # each in one pool, automatic plan, as for the headline.
+    configs = None
+    if not args.no_configs:
+        t5 = time.time()
+        configs = {}
+        Lc = 8
+        for wid in (1, 2, 4):
+            wl, base = [], 0
+            for l in range(Lc):
+                w = W.make(wid, layer=l, page_base=base)
+                wl.append(w)
+                base = w.pool_pages
+            cpool = torch.zeros(base * W.PAGE * wl[0].row_bytes, dtype=torch.uint8, device=dev)
+            dl = [upload(w, dev, pool=cpool) for w in wl]
+            shapes = [smla.make_shape(w.B, w.kv_format, w.page_table.shape[1], base) for w in wl]
+            cplan, cwsb = smla.plan_for(shapes[0])
+            cws = smla.new_workspace(cwsb, dev)
+            co = torch.empty((wl[0].B, 64, 512), dtype=torch.bfloat16, device=dev)
+            cl = torch.empty((wl[0].B, 64), dtype=torch.float32, device=dev)
+
+            def ccall(k):
+                call(dl[k % Lc], shapes[k % Lc], cplan, cws, co, cl)
+            for k in range(10):
+                ccall(k)
+            us = statistics.median(timed(ccall, args.sweep_steps) for _ in range(3))
+            cb = float(np.mean([algorithmic(w)[0] for w in wl]))
+            cf = float(np.mean([algorithmic(w)[1] for w in wl]))
+            configs[wl[0].name] = {
+                "B": wl[0].B, "kv_format": "bf16" if wl[0].kv_format == W.FMT_BF16 else "fp8", "us_per_layer": round(us, 2),
+                "plan": cplan.as_dict(), "algorithmic_bytes": int(cb), "GBps": round(cb / (us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "mfma_frac_bf16_peak": round(cf / (us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4)}
+            del dl, cpool, cws
+            torch.cuda.empty_cache()
+        log(f"other workloads done in {time.time() - t5:.1f}s: "
+            f"{ {k: (v['us_per_layer'], v['hbm_frac']) for k, v in configs.items()} }")
 
     # ------------------------------------------------------------------ query tokens
     # q_len query tokens per request sharing its selection, on the same cold
@@ -460,6 +502,7 @@ def main() -> int:
             "sweep": sweep,
             "indexer_topk": indexer,
             "selector_check": selector,
+            "other_workloads": configs,
             "kv_append": None if append is None else {
                 "kernel": "append_kernel<1>", "format": "fp8 rows from fp32 latent/rope", "requests": 80,
                 "per_n_tokens": append},
