@@ -186,6 +186,11 @@ def main() -> int:
             for _ in range(args.repeats)]
     full_us = statistics.median(runs)
     log(f"B={B} plan={plan.as_dict()} us/call per repeat: {[round(r, 2) for r in runs]}")
+    # input set 0's result, compared with the oracle in the CPU-baseline leg
+    call(sets[0][1], shape, plan, ws, out, lse)
+    torch.cuda.synchronize()
+    out0 = out.float().cpu().numpy().astype(np.float64)
+    lse0 = lse.cpu().numpy().astype(np.float64)
 
     alg = [algorithmic(w) for w, _ in sets]
     call_bytes = float(np.mean([a[0] for a in alg]))
@@ -462,6 +467,7 @@ def main() -> int:
 
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         import oracle
         hp = w0.host_pool()
@@ -476,6 +482,15 @@ def main() -> int:
         cpu = {"value": round(el / n * 1e6, 1), "unit": "us/layer", "cores": oracle.max_threads(), "kind": "oracle",
                "sample": f"fp64 C oracle (OpenMP over request x head) on input set 0 of {w0.name} "
                          f"(B={w0.B}, whole batch), {n} calls in {el:.1f}s"}
+        # the timed kernel's output on that set against the oracle's: per (request, head) row the largest
+        # difference over the row's largest magnitude, and the largest lse difference
+        ref_o, ref_l = oracle.decode_workload(w0, pool=hp)
+        den = np.maximum(np.abs(ref_o).max(axis=-1), 1e-30)
+        parity = {"input_set": 0, "rows": int(den.size), "tolerance": 6.7e-3,
+                  "max_rel_err": float((np.abs(out0 - ref_o).max(axis=-1) / den).max()),
+                  "max_abs_dlse": float(np.abs(np.where(lse0 == ref_l, 0.0, lse0 - ref_l)).max())}   # -inf == -inf
+        parity["within_tolerance"] = parity["max_rel_err"] <= 6.7e-3 and parity["max_abs_dlse"] <= 6.7e-3
+        log(f"parity against the oracle: {parity}")
 
     res = {
         "metric": METRIC,
@@ -503,6 +518,7 @@ def main() -> int:
             "indexer_topk": indexer,
             "selector_check": selector,
             "other_workloads": configs,
+            "parity_vs_oracle": parity,
             "kv_append": None if append is None else {
                 "kernel": "append_kernel<1>", "format": "fp8 rows from fp32 latent/rope", "requests": 80,
                 "per_n_tokens": append},
