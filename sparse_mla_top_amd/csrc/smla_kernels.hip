@@ -80,106 +80,75 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       : "m0");
 }
 
-// Layout of a tile (kTile = 32 rows of kRow / 16 chunks of 16 bytes) in LDS.
-// Chunks go in groups of four; the 16 rows x 4 chunks of a row half and a
-// chunk group form one 1 KB block, in which the 16 rows of each chunk are
-// contiguous:
-//   slot(row, chunk) = ((chunk / 4) * 2 + row / 16) * 64 + (chunk % 4) * 16 + row % 16
-// A ds_read_b128 runs at the full 256 B/clk only when each 16 consecutive
-// lanes read one contiguous 256-byte span; the QK operand reads (16 lanes =
-// 16 rows of one chunk) do here, where rows 656 bytes apart conflict two-way.
-// Each direct-to-LDS instruction fills one block (16 rows x 64 bytes).  A
-// 41-chunk fp8 row leaves one chunk after its 10 groups: it takes a 32-slot
-// tail, slot 1280 + row.
+// Layout of a tile (kTile = 32 rows of kRow bytes) in LDS: the rows packed
+// one after another, exactly as they sit in a cache row, so slot s (16 bytes)
+// holds chunk s % kChunksRow of row s / kChunksRow.  Each direct-to-LDS
+// instruction fills 64 consecutive slots, so its 64 lanes read one to three
+// rows' contiguous bytes: few cache lines per instruction, which is what sets
+// the gather rate of a compute unit (a layout where one instruction touched
+// 16 rows x 64 bytes gathered 2.4x slower on L2 hits).  The operand reads of
+// the QK and PV waves run at nearly the rate of a contiguous layout on this
+// row stride (656 = 164 dwords: the 16 rows a 16-lane group reads fall on
+// distinct bank quads).
 template <int FMT> struct TileLayout {
   static constexpr int kChunksRow = RowFmt<FMT>::kRow / 16;   // 41 (fp8) or 72 (bf16)
-  static constexpr int kGroups = kChunksRow / 4;
-  static constexpr int kTail = kGroups * 128;                 // first slot after the groups
   static constexpr int kSlots = kTile * kChunksRow;
+  static constexpr int kInstr = (kSlots + 63) / 64;           // 21 (fp8; the last one half full) or 36
   __device__ static constexpr uint32_t off(int row, int chunk) {   // byte offset in the tile
-    return 16u * (uint32_t)(chunk < 4 * kGroups ? ((chunk >> 2) * 2 + (row >> 4)) * 64 + (chunk & 3) * 16 + (row & 15)
-                                                : kTail + (chunk - 4 * kGroups) * kTile + row);
-  }
-  __host__ __device__ static constexpr int row_of(int slot) {
-    return slot < kTail ? 16 * ((slot >> 6) & 1) + (slot & 15) : (slot - kTail) % kTile;
-  }
-  __host__ __device__ static constexpr int chunk_of(int slot) {
-    return slot < kTail ? 4 * (slot >> 7) + ((slot >> 4) & 3) : 4 * kGroups + (slot - kTail) / kTile;
+    return (uint32_t)(row * RowFmt<FMT>::kRow + 16 * chunk);
   }
 };
 
-// Issue the direct-to-LDS loads of one tile: slot s of the layout above takes
-// chunk chunk_of(s) of row row_of(s), read from that row's address (the zero
-// row when the slot is masked; bit 0 of the address marks that).  Issuing
-// wave v (0..3) takes load instructions v, v+4, ... of the tile; the count
-// per wave is DmaCount<FMT>::of(v).
-//
-// Instruction j < 2 kGroups fills slots 64j + lane: row 16 (j & 1) + lane % 16,
-// chunk 4 (j >> 1) + lane / 16.  A wave's instructions all have j & 1 = v & 1,
-// so each lane reads one row for all of them, at offsets 64 (j >> 1) past its
-// chunk; the tail instruction (fp8 rows) reads row lane % 32 of the chunks
-// after the groups.  TileSrc holds those two per-lane addresses, so they can
-// be read from LDS a tile ahead of the loads.
-struct TileSrc {
-  uint64_t main, tail;   // row addresses as stored (bit 0: masked row)
+// Issue the direct-to-LDS loads of one tile.  Instruction j fills slots
+// 64j .. 64j + 63: lane l reads chunk (64j + l) % kChunksRow of row
+// (64j + l) / kChunksRow from that row's address (the zero row when the slot
+// is masked; bit 0 of the stored address marks that).  Issuing wave v
+// (0 .. kPvWaves-1) takes instructions v, v + kPvWaves, ...; the count per
+// wave is DmaCount<FMT>::of(v).
+// TileSrc holds the wave's per-lane source addresses of one tile, read from
+// LDS a tile ahead of the loads (lanes past the last slot hold 0 and issue
+// nothing).
+template <int FMT> struct DmaCount {
+  static constexpr int kInstr = TileLayout<FMT>::kInstr;
+  // issuing wave v (0 .. kPvWaves-1) takes instructions v, v + kPvWaves, ...
+  __host__ __device__ static constexpr int of(int v) { return (kInstr - v + kPvWaves - 1) / kPvWaves; }
+  // waves 0 .. kRichWaves-1 issue of(0) loads per tile, the rest of(kPvWaves - 1)
+  static constexpr int kRichWaves = (kInstr % kPvWaves == 0) ? kPvWaves : kInstr % kPvWaves;
+  static constexpr int kPerWave = of(0);
+  static constexpr int kPoor = of(kPvWaves - 1);
+};
+static_assert(DmaCount<kFmtFp8>::of(DmaCount<kFmtFp8>::kRichWaves - 1) == DmaCount<kFmtFp8>::of(0), "");
+static_assert(DmaCount<kFmtBf16>::of(DmaCount<kFmtBf16>::kRichWaves - 1) == DmaCount<kFmtBf16>::of(0), "");
+
+template <int FMT> struct TileSrc {
+  uint64_t a[DmaCount<FMT>::kPerWave];   // source of this lane's 16 bytes in instruction v + kPvWaves q
 };
 template <int FMT>
-__device__ __forceinline__ TileSrc tile_src(const uint64_t LDS_AS* rowaddr_s, int tok0, int v, int lane) {
+__device__ __forceinline__ TileSrc<FMT> tile_src(const uint64_t LDS_AS* rowaddr_s, int tok0, int v, int lane) {
   using TL = TileLayout<FMT>;
-  constexpr int kFull = 2 * TL::kGroups;
-  constexpr int kInstr = (TL::kSlots + 63) / 64;
-  static_assert(TL::kSlots - TL::kTail <= 64, "at most one tail instruction");
-  TileSrc s;
-  s.main = rowaddr_s[tok0 + 16 * (v & 1) + (lane & 15)];
-  s.tail = 0;
-  if (kInstr > kFull && v == kFull % 4) s.tail = rowaddr_s[tok0 + (lane & 31)];
+  TileSrc<FMT> s;
+#pragma unroll
+  for (int q = 0; q < DmaCount<FMT>::kPerWave; ++q) {
+    const int slot = 64 * (v + kPvWaves * q) + lane;
+    const int row = slot / TL::kChunksRow, chunk = slot - row * TL::kChunksRow;
+    s.a[q] = slot < TL::kSlots ? (rowaddr_s[tok0 + row] & ~1ull) + 16 * chunk : 0;
+  }
   return s;
 }
-// The per-lane addresses above cover the layout exactly (checked over every slot).
-template <int FMT> constexpr bool tile_src_covers_layout() {
-  using TL = TileLayout<FMT>;
-  for (int slot = 0; slot < TL::kSlots; ++slot) {
-    const int j = slot / 64, lane = slot % 64;
-    const bool full = j < 2 * TL::kGroups;
-    const int row = full ? 16 * (j & 1) + lane % 16 : lane % 32;
-    const int chunk = full ? 4 * (j >> 1) + lane / 16 : 4 * TL::kGroups + lane / 32;
-    if (row != TL::row_of(slot) || chunk != TL::chunk_of(slot)) return false;
-  }
-  return true;
-}
-static_assert(tile_src_covers_layout<kFmtFp8>() && tile_src_covers_layout<kFmtBf16>(), "tile source layout");
 template <int FMT>
-__device__ __forceinline__ void issue_tile(const TileSrc& s, uint8_t LDS_AS* lds, int v, int lane) {
+__device__ __forceinline__ void issue_tile(const TileSrc<FMT>& s, uint8_t LDS_AS* lds, int v, int lane) {
   using TL = TileLayout<FMT>;
-  constexpr int kFull = 2 * TL::kGroups;
-  constexpr int kInstr = (TL::kSlots + 63) / 64;
-  constexpr int kPerWave = (kInstr + 3) / 4;
-  const uint64_t main = (s.main & ~1ull) + 16 * (lane >> 4);
-  const uint64_t tail = (s.tail & ~1ull) + 16 * (4 * TL::kGroups + (lane >> 5));
 #pragma unroll
-  for (int q = 0; q < kPerWave; ++q) {
-    const int j = v + 4 * q;
-    if (j < kFull)
-      dma16((const void*)(uintptr_t)(main + 64 * (j >> 1)), (uint32_t)(uintptr_t)(lds + j * 64 * 16));
-    else if (j < kInstr && lane < TL::kSlots - TL::kTail)
-      dma16((const void*)(uintptr_t)tail, (uint32_t)(uintptr_t)(lds + j * 64 * 16));
+  for (int q = 0; q < DmaCount<FMT>::kPerWave; ++q) {
+    const int j = v + kPvWaves * q;
+    if (j < TL::kInstr && 64 * j + lane < TL::kSlots)   // the last fp8 instruction fills 32 slots
+      dma16((const void*)(uintptr_t)s.a[q], (uint32_t)(uintptr_t)(lds + j * 64 * 16));
   }
 }
 
 // Raw V^T operand of one PV MFMA as read from LDS: 8 fp8 codes or 8 bf16.
 template <int FMT> struct VRaw { typedef i32x2 type; };
 template <> struct VRaw<kFmtBf16> { typedef i32x4 type; };
-
-template <int FMT> struct DmaCount {
-  static constexpr int kChunks = kTile * (RowFmt<FMT>::kRow / 16);
-  static constexpr int kInstr = (kChunks + 63) / 64;
-  // issuing wave v (0..3) takes instructions v, v+4, ...
-  __host__ __device__ static constexpr int of(int v) { return (kInstr - v + 3) / 4; }
-  // waves 0 .. kRichWaves-1 issue of(0) loads per tile, the rest of(3)
-  static constexpr int kRichWaves = (kInstr % 4 == 0) ? 4 : kInstr % 4;
-};
-static_assert(DmaCount<kFmtFp8>::of(DmaCount<kFmtFp8>::kRichWaves - 1) == DmaCount<kFmtFp8>::of(0), "");
-static_assert(DmaCount<kFmtBf16>::of(DmaCount<kFmtBf16>::kRichWaves - 1) == DmaCount<kFmtBf16>::of(0), "");
 
 // s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
@@ -341,7 +310,10 @@ __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, co
                                             float* wt) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
-  const int vb = wave >> 1, db0 = 2 * (wave & 1);
+  // waves 0..7 each merge the 16 runs (vb, db0 .. db0 + 1, *); the others only
+  // take part in the barriers
+  const bool mw = wave < 8;
+  const int vb = mw ? wave >> 1 : 0, db0 = 2 * (wave & 1);
   const int nother = nsplit - 1;
   auto other = [&](int k) { return k < own ? k : k + 1; };    // k-th split other than own, ascending
   const float* ls = part_lse + (int64_t)b * nsplit * kHeads + kHpw * hb;
@@ -349,17 +321,18 @@ __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, co
   // lse of every split for the group's 32 heads (one per thread), issued first
   const int sp_l = t >> 5, h_l = t & (kHpw - 1);
   const float lv = sp_l < nsplit ? (sp_l == own ? own_lse[h_l] : load_agent(ls + sp_l * kHeads + h_l)) : 0.f;
-  f32x4 v[4][2][4];
+  constexpr int kRound = 2;   // partials loaded per round (2 x 32 registers in flight)
+  f32x4 v[kRound][2][4];
   auto issue = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kRound; ++u)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          v[u][i][j] = k0 + u < nother ? load_run(part_o, (int64_t)b * nsplit + other(k0 + u),
-                                                  part_run_offset(vb, db0 + i, j, hb, lane))
-                                       : f32x4{0.f, 0.f, 0.f, 0.f};
+          v[u][i][j] = mw && k0 + u < nother ? load_run(part_o, (int64_t)b * nsplit + other(k0 + u),
+                                                        part_run_offset(vb, db0 + i, j, hb, lane))
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   issue(0);
   if (sp_l < nsplit) wt[t] = lv;
@@ -368,6 +341,7 @@ __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, co
     lse[(int64_t)b * kHeads + kHpw * hb + t] =
         split_weights(nsplit, [&](int sp) { return wt[sp * kHpw + t]; }, wt + t, kHpw);
   lds_barrier();
+  if (!mw) return;   // no barrier follows
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -385,10 +359,10 @@ __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, co
     return *reinterpret_cast<const f32x4*>(own_part + part_run_offset(vb, db0 + i, j, hb, lane));
   };
   bool own_done = false;
-  for (int k0 = 0; k0 < nother; k0 += 4) {
+  for (int k0 = 0; k0 < nother; k0 += kRound) {
     if (k0 > 0) issue(k0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRound; ++u) {
       if (k0 + u >= nother) break;
       const int sp = other(k0 + u);
       if (!own_done && own < sp) {
@@ -470,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4;          // row group of MFMA layouts
   const int c16 = lane & 15;        // column within a 16-wide MFMA tile
-  const bool qk_role = wave < 4;
+  const bool qk_role = wave < kQkWaves;
 
   // work item -> (request, split, query token, head group).  The q_len query
   // tokens of a request share its selected rows; all 2 * q_len workgroups of
@@ -519,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 
   // ---- 3. the PV waves issue every tile load (the QK waves never wait on
   // the texture path)
-  const int vwave = wave & 3;
+  const int vwave = qk_role ? 0 : wave - kQkWaves;     // PV wave 0 .. kPvWaves-1
   // In iteration k the QK waves start tile k+1 and finish tile k, and the PV
   // waves accumulate tile k-1; tile k + kAhead is issued in iteration k
   // into the buffer of tile k - 2 (finished at k - 2, accumulated at k - 1,
@@ -535,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // behind the others' later ones).  The rest follow one per iteration.
   const int npre = min(kAhead, ntiles);
   auto src_of = [&](int tt) { return tile_src<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile, vwave, lane); };
-  auto issue = [&](int tt, const TileSrc& src) {
+  auto issue = [&](int tt, const TileSrc<FMT>& src) {
     issue_tile<FMT>(src, (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), vwave, lane);
   };
   if (!qk_role)
@@ -550,10 +524,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     if (need < ntiles) {
       const int after = issued - need - 1;                    // tiles issued after it
       if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(after);
-      else wait_tiles<DmaCount<FMT>::of(3)>(after);
+      else wait_tiles<DmaCount<FMT>::kPoor>(after);
     } else if (k < ntiles) {
       if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(0);
-      else wait_tiles<DmaCount<FMT>::of(3)>(0);
+      else wait_tiles<DmaCount<FMT>::kPoor>(0);
     }
   };
 
@@ -644,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     };
     struct KOps {                           // K operands of one tile (fp8 rows)
       i32x8 ka[4];                          // codes 128blk + 32g .. +31
-      bf16x8 kr[2];                         // rope dims 32c + 8g .. +7
+      const uint8_t* tb;                    // the tile (its rope dims are read at the MFMAs)
     };
     auto read_k = [&](int kt, KOps& o) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
@@ -655,19 +629,23 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         const i32x4 k1 = *reinterpret_cast<const i32x4*>(tb + TL::off(row, 8 * blk + 2 * g + 1));
         o.ka[blk] = i32x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
       }
-      // rope dims 32c + 8g .. +7 sit at byte 528 + 2 (32c + 8g): chunk 33 + 4c + g
-#pragma unroll
-      for (int c = 0; c < 2; ++c) o.kr[c] = *reinterpret_cast<const bf16x8*>(tb + TL::off(row, 33 + 4 * c + g));
+      o.tb = tb;
     };
     auto mfma_scores = [&](const KOps& o, Raw& r) {
-      // independent MFMA chains: hi of every block, rope, then lo
+      // independent MFMA chains: hi of every block, rope, then lo.  The rope
+      // dims 32c + 8g .. +7 (byte 528 + 2 (32c + 8g): chunk 33 + 4c + g) are
+      // read here, their latency under the hi MFMAs, so they take no
+      // registers across the softmax.
+      bf16x8 kr[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) kr[c] = *reinterpret_cast<const bf16x8*>(o.tb + TL::off(row, 33 + 4 * c + g));
       f32x4 sm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk)
         r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.ka[blk], qhi[blk], f32x4{0.f, 0.f, 0.f, 0.f},
                                                                      0, 0, 0, 0, 0, 0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.kr[c], qb[16 + c], sm, 0, 0, 0);
+      for (int c = 0; c < 2; ++c) sm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[c], qb[16 + c], sm, 0, 0, 0);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk)
         r.acc[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(o.ka[blk], qlo[blk], r.acc[blk], 0, 0, 0, 0, 0, 0);
@@ -773,14 +751,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         if (!dry) lds_barrier();
       }
     };
-    Raw ra, rb;
+    Raw ra;   // one buffer: tile k's raw scores are consumed before tile k+1's MFMAs overwrite them
     const int kfirst = __builtin_amdgcn_readfirstlane(a.nsplit > 0 ? -1 : 0);
     if constexpr (kPipe) {
       // unrolled by two so the raw scores alternate between ra and rb
 #pragma clang loop unroll(disable)
       for (int k = kfirst; k < ntiles; k += 2) {
-        body(k, ra, rb);
-        if (k + 1 < ntiles) body(k + 1, rb, ra);
+        body(k, ra, ra);
+        if (k + 1 < ntiles) body(k + 1, ra, ra);
       }
     } else {
 #pragma clang loop unroll(disable)
@@ -817,15 +795,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // one accumulator per 16-token half (each half has its own running max).
     // Operand lane layout (both): row/col = lane % 32, k = 8 * (lane / 32) + i,
     // so k-slot (lane/32, i) of half kh is token 16kh + 8(lane/32) + i.
-    const int vb = wave - 4;          // scale block / 128-dim slice of the latent
+    const int pw = wave - kQkWaves;   // PV wave 0 .. 7
+    const int vb = pw >> 1;           // scale block (128-dim slice of the latent) ...
+    const int dh = pw & 1;            // ... and which 64-dim half of it this wave owns
     const int l32 = lane & 31, kg = lane >> 5;
-    f32x16 o[4][2];                   // [32-dim block of the slice][token half]
+    f32x16 o[2][2];                   // [32-dim block of the half-slice][token half]
     // zero from an asm statement, so the compiler cannot hoist the zeroing
     // above the role branch and keep 128 registers live through the QK path
     float zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) o[i][j] = zero;
 
@@ -834,24 +814,25 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // MFMAs of tile k-1), so their latency hides under the MFMAs and the
     // barrier.  Tile k is published by the barrier of iteration k - 1 (k when
     // unpipelined) and its buffer is reloaded only in iteration k + 2.
-    typename VRaw<FMT>::type vnext[2][4];
+    typename VRaw<FMT>::type vnext[2][2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vnext[kh][db] = {};
+      for (int dl = 0; dl < 2; ++dl) vnext[kh][dl] = {};
     auto read_v = [&](int kt) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const int gg = lane >> 4;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int dl = 0; dl < 2; ++dl) {
+          const int db = 2 * dh + dl;   // 32-dim block within the scale block
           if constexpr (FMT == kFmtFp8) {
             // 16-lane group gg reads tokens 16kh + 8(gg>>1) + 0..7 x dims
             // 32db + 16(gg&1) + 0..15; source lane (2r + half) supplies 8 bytes of row r
             const int r = c16 >> 1, half = c16 & 1;
             const uint8_t* src = tb + TL::off(16 * kh + 8 * (gg >> 1) + r, 8 * vb + 2 * db + (gg & 1)) + 8 * half;
-            vnext[kh][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
+            vnext[kh][dl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
           } else {
             // two 4-row reads per group: rows 16kh + 8(gg>>1) + 0..3 and + 4..7;
             // source lane (4r + q) supplies 4 elements of row r
@@ -865,12 +846,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
             // result were mis-lowered (the upper dword was dropped)
             const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
             const i32x2 a1 = __builtin_bit_cast(i32x2, r1);
-            vnext[kh][db] = i32x4{a0[0], a0[1], a1[0], a1[1]};
+            vnext[kh][dl] = i32x4{a0[0], a0[1], a1[0], a1[1]};
           }
         }
     };
 
-    TileSrc nsrc{0, 0};               // load sources of the next tile to issue
+    TileSrc<FMT> nsrc{};              // load sources of the next tile to issue
     // Iteration 0 has no P yet: it is a warm-up pass through the same loop
     // code on zero operands and an unwritten P buffer (loading the
     // instructions into the cache while the QK waves score tile 0); its
@@ -897,24 +878,24 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       for (int kh = 0; kh < 2; ++kh)
         if (__builtin_amdgcn_ballot_w64(al[kh] != 1.0f)) {
 #pragma unroll
-          for (int db = 0; db < 4; ++db) o[db][kh] *= al[kh];
+          for (int dl = 0; dl < 2; ++dl) o[dl][kh] *= al[kh];
         }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int dl = 0; dl < 2; ++dl) {
           bf16x8 va;
           if constexpr (FMT == kFmtFp8) {
-            const i32x2 raw = vnext[kh][db];
+            const i32x2 raw = vnext[kh][dl];
             va = fp8x8_to_bf16((uint64_t)(uint32_t)raw[0] | ((uint64_t)(uint32_t)raw[1] << 32));
           } else {
-            va = __builtin_bit_cast(bf16x8, vnext[kh][db]);
+            va = __builtin_bit_cast(bf16x8, vnext[kh][dl]);
           }
-          o[db][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[kh], o[db][kh], 0, 0, 0);
+          o[dl][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[kh], o[dl][kh], 0, 0, 0);
         }
       if (dry) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
       }
@@ -925,12 +906,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       // direct-to-LDS instruction is slow to leave the issue queue, and the
       // MFMAs run meanwhile.  Its buffer held tile k - 2, done with by every
       // wave before this iteration's barrier.
+      // The next tile's sources are read a tile ahead (fp8 rows: 6 registers;
+      // bf16 rows: 10) so the loads go out without waiting on LDS.
+      constexpr bool kSrcAhead = true;
       if (k == 0) {
         for (int tt = npre; tt <= kAhead && tt < ntiles; ++tt) issue(tt, src_of(tt));
-        if (kAhead + 1 < ntiles) nsrc = src_of(kAhead + 1);
+        if (kSrcAhead && kAhead + 1 < ntiles) nsrc = src_of(kAhead + 1);
       } else if (k + kAhead < ntiles) {
-        issue(k + kAhead, nsrc);
-        if (k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
+        issue(k + kAhead, kSrcAhead ? nsrc : src_of(k + kAhead));
+        if (kSrcAhead && k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
       }
     }
 
@@ -951,46 +935,47 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       lse_v = Lh > 0.f ? (M + __builtin_amdgcn_logf(Lh)) * kLn2 : -INFINITY;
     }
     const int ghead = kHpw * hg + l32;
-    if (vb == 0 && kg == 0) {
+    if (pw == 0 && kg == 0) {
       lsev_s[l32] = lse_v;
       if (a.nsplit == 1) a.lse[(int64_t)vr * kHeads + ghead] = lse_v;
       else if (!(fused && last_s)) store_agent(a.part_lse + ((int64_t)vr * a.nsplit + s) * kHeads + ghead, lse_v);
     }
-    // register j of o[db][*] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head l32]
-    f32x16 res[4];
+    // register j of o[dl][*] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head l32], db = 2dh + dl
+    f32x16 res[2];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) res[db] = o[db][0] * f[0] + o[db][1] * f[1];
+    for (int dl = 0; dl < 2; ++dl) res[dl] = o[dl][0] * f[0] + o[dl][1] * f[1];
     if (a.nsplit == 1) {
       uint16_t* orow = a.out + ((int64_t)vr * kHeads + ghead) * kDv + 128 * vb + 4 * kg;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[db][4 * jj]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[db][4 * jj + 2]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 3]) << 16);
-          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[dl][4 * jj]) | ((uint32_t)f32_to_bf16_rne(res[dl][4 * jj + 1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[dl][4 * jj + 2]) | ((uint32_t)f32_to_bf16_rne(res[dl][4 * jj + 3]) << 16);
+          *reinterpret_cast<uint2*>(orow + 32 * (2 * dh + dl) + 8 * jj) = make_uint2(lo, hi);
         }
     } else if (!fused || !last_s) {
       const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)vr * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 v = {res[db][4 * jj], res[db][4 * jj + 1], res[db][4 * jj + 2], res[db][4 * jj + 3]};
+          const f32x4 v = {res[dl][4 * jj], res[dl][4 * jj + 1], res[dl][4 * jj + 2], res[dl][4 * jj + 3]};
+          const uint32_t off = part_run_offset(vb, 2 * dh + dl, jj, hg, lane);
           if (fused)   // read back in this launch, possibly on another XCD
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hg, lane), 0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSc1);
           else         // read by the combine launch
-            __builtin_amdgcn_raw_buffer_store_b128(v, r, part_run_offset(vb, db, jj, hg, lane), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
         }
     } else {
       // last split of this (request, head group): its own partial goes to
       // LDS, at the offsets it has in a workspace block
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, db, jj, hg, lane)) =
-              f32x4{res[db][4 * jj], res[db][4 * jj + 1], res[db][4 * jj + 2], res[db][4 * jj + 3]};
+          *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, 2 * dh + dl, jj, hg, lane)) =
+              f32x4{res[dl][4 * jj], res[dl][4 * jj + 1], res[dl][4 * jj + 2], res[dl][4 * jj + 3]};
     }
   }
 
