@@ -16,9 +16,10 @@ constexpr int kTopk = 512;
 constexpr int kPage = 64;
 constexpr int kTile = 32;       // tokens per pipeline tile
 constexpr int kTiles = kTopk / kTile;
-constexpr int kQkWaves = 4;     // split kernel: 4 QK waves (16 heads x 16-token half each)
-constexpr int kPvWaves = 8;     // + 8 PV waves (64 latent dims each), which also issue the row loads
-constexpr int kWaves = kQkWaves + kPvWaves;
+constexpr int kQkWaves = 4;     // split kernel: 4 QK waves (16 heads x 16-token half each),
+constexpr int kPvWaves = 4;     // 4 PV waves (128 latent dims each)
+constexpr int kLdWaves = 4;     // and 4 loader waves that issue the row loads
+constexpr int kWaves = kQkWaves + kPvWaves + kLdWaves;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFmtBf16 = 0;
 constexpr int kFmtFp8 = 1;

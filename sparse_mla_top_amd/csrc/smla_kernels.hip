@@ -102,45 +102,44 @@ template <int FMT> struct TileLayout {
 // Issue the direct-to-LDS loads of one tile.  Instruction j fills slots
 // 64j .. 64j + 63: lane l reads chunk (64j + l) % kChunksRow of row
 // (64j + l) / kChunksRow from that row's address (the zero row when the slot
-// is masked; bit 0 of the stored address marks that).  Issuing wave v
-// (0 .. kPvWaves-1) takes instructions v, v + kPvWaves, ...; the count per
-// wave is DmaCount<FMT>::of(v).
+// is masked; bit 0 of the stored address marks that).  With NW issuing
+// waves, wave v (0 .. NW-1) takes instructions v, v + NW, ...; its count per
+// tile is DmaCount<FMT, NW>::of(v).
 // TileSrc holds the wave's per-lane source addresses of one tile, read from
 // LDS a tile ahead of the loads (lanes past the last slot hold 0 and issue
 // nothing).
-template <int FMT> struct DmaCount {
+template <int FMT, int NW> struct DmaCount {
   static constexpr int kInstr = TileLayout<FMT>::kInstr;
-  // issuing wave v (0 .. kPvWaves-1) takes instructions v, v + kPvWaves, ...
-  __host__ __device__ static constexpr int of(int v) { return (kInstr - v + kPvWaves - 1) / kPvWaves; }
-  // waves 0 .. kRichWaves-1 issue of(0) loads per tile, the rest of(kPvWaves - 1)
-  static constexpr int kRichWaves = (kInstr % kPvWaves == 0) ? kPvWaves : kInstr % kPvWaves;
+  // issuing wave v (0 .. NW-1) takes instructions v, v + NW, ...
+  __host__ __device__ static constexpr int of(int v) { return (kInstr - v + NW - 1) / NW; }
+  // waves 0 .. kRichWaves-1 issue of(0) loads per tile, the rest of(NW - 1)
+  static constexpr int kRichWaves = (kInstr % NW == 0) ? NW : kInstr % NW;
   static constexpr int kPerWave = of(0);
-  static constexpr int kPoor = of(kPvWaves - 1);
+  static constexpr int kPoor = of(NW - 1);
+  __device__ static constexpr int per(int v) { return v < kRichWaves ? kPerWave : kPoor; }
 };
-static_assert(DmaCount<kFmtFp8>::of(DmaCount<kFmtFp8>::kRichWaves - 1) == DmaCount<kFmtFp8>::of(0), "");
-static_assert(DmaCount<kFmtBf16>::of(DmaCount<kFmtBf16>::kRichWaves - 1) == DmaCount<kFmtBf16>::of(0), "");
 
-template <int FMT> struct TileSrc {
-  uint64_t a[DmaCount<FMT>::kPerWave];   // source of this lane's 16 bytes in instruction v + kPvWaves q
+template <int FMT, int NW> struct TileSrc {
+  uint64_t a[DmaCount<FMT, NW>::kPerWave];   // source of this lane's 16 bytes in instruction v + NW q
 };
-template <int FMT>
-__device__ __forceinline__ TileSrc<FMT> tile_src(const uint64_t LDS_AS* rowaddr_s, int tok0, int v, int lane) {
+template <int FMT, int NW>
+__device__ __forceinline__ TileSrc<FMT, NW> tile_src(const uint64_t LDS_AS* rowaddr_s, int tok0, int v, int lane) {
   using TL = TileLayout<FMT>;
-  TileSrc<FMT> s;
+  TileSrc<FMT, NW> s;
 #pragma unroll
-  for (int q = 0; q < DmaCount<FMT>::kPerWave; ++q) {
-    const int slot = 64 * (v + kPvWaves * q) + lane;
+  for (int q = 0; q < DmaCount<FMT, NW>::kPerWave; ++q) {
+    const int slot = 64 * (v + NW * q) + lane;
     const int row = slot / TL::kChunksRow, chunk = slot - row * TL::kChunksRow;
     s.a[q] = slot < TL::kSlots ? (rowaddr_s[tok0 + row] & ~1ull) + 16 * chunk : 0;
   }
   return s;
 }
-template <int FMT>
-__device__ __forceinline__ void issue_tile(const TileSrc<FMT>& s, uint8_t LDS_AS* lds, int v, int lane) {
+template <int FMT, int NW>
+__device__ __forceinline__ void issue_tile(const TileSrc<FMT, NW>& s, uint8_t LDS_AS* lds, int v, int lane) {
   using TL = TileLayout<FMT>;
 #pragma unroll
-  for (int q = 0; q < DmaCount<FMT>::kPerWave; ++q) {
-    const int j = v + kPvWaves * q;
+  for (int q = 0; q < DmaCount<FMT, NW>::kPerWave; ++q) {
+    const int j = v + NW * q;
     if (j < TL::kInstr && 64 * j + lane < TL::kSlots)   // the last fp8 instruction fills 32 slots
       dma16((const void*)(uintptr_t)s.a[q], (uint32_t)(uintptr_t)(lds + j * 64 * 16));
   }
@@ -155,6 +154,17 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0 .. N (the immediate is
+// chosen by a chain of scalar compares).
+template <int N> __device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<N>();
+    else wait_vmcnt_le<N - 1>(n);
+  }
+}
+
 // Wait until at most `tiles_after` tiles' worth of this wave's loads are
 // outstanding (loads complete in issue order), i.e. every earlier tile landed.
 template <int PER_TILE>
@@ -472,9 +482,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int hq = wave & 1, mh = (wave >> 1) & 1;
   const int hloc = 16 * hq + c16;                          // head within the group
   const int head = kHpw * hg + hloc;                       // head of the request
-  // ---- 2. index translation, one token per thread
-  {
-    const int t = threadIdx.x;
+  // ---- 2. Q and index translation.  The QK waves request their heads' raw
+  // Q at once, while the other eight waves translate (one token per thread),
+  // so Q streams in during the two dependent index loads instead of sharing
+  // the compute unit's memory path with the first tiles.
+  if (!qk_role) {
+    const int tw = wave - kQkWaves;                 // translating wave 0 .. 7
+    const int t = threadIdx.x - 64 * kQkWaves;      // token 0 .. 511
     bool valid = false;
     if (t < ntok) {
       const int64_t slot = translate(a.page_table, a.topk_idx, ctx, b, tile0 * kTile + t, a.max_pages,
@@ -484,75 +498,99 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
                            : ((uint64_t)(uintptr_t)g_zero_row | 1ull);
     }
     const uint64_t bits = __builtin_amdgcn_ballot_w64(valid);
-    if (lane == 0 && 2 * wave < kTiles) {
-      mask_s[2 * wave] = (uint32_t)bits;
-      mask_s[2 * wave + 1] = (uint32_t)(bits >> 32);
+    if (lane == 0 && 2 * tw < kTiles) {
+      mask_s[2 * tw] = (uint32_t)bits;
+      mask_s[2 * tw + 1] = (uint32_t)(bits >> 32);
     }
+    lds_barrier();   // the QK waves take the same barrier in their own branch below
   }
-  lds_barrier();
+  static_assert(64 * (kPvWaves + kLdWaves) >= kTopk, "the translating waves cover every top-k slot");
 
-  // ---- 3. the PV waves issue every tile load (the QK waves never wait on
-  // the texture path)
-  const int vwave = qk_role ? 0 : wave - kQkWaves;     // PV wave 0 .. kPvWaves-1
+  // ---- 3. row loads.  The first npre tiles go out at once, issued by the PV
+  // and loader waves together; every later tile is issued by the loader waves
+  // alone, one per iteration.  A direct-to-LDS load holds its issuing wave
+  // for a long time when the memory path is busy, so no wave that computes
+  // issues a load inside the loop.
+  const bool ld_role = wave >= kQkWaves + kPvWaves;
+  const int iw = qk_role ? 0 : wave - kQkWaves;             // first-burst issuer 0 .. 7
+  const int lw = ld_role ? wave - kQkWaves - kPvWaves : 0;  // loader 0 .. 3
+  constexpr int kInitIssuers = kPvWaves + kLdWaves;
+  using InitDma = DmaCount<FMT, kInitIssuers>;
+  using LdDma = DmaCount<FMT, kLdWaves>;
   // In iteration k the QK waves start tile k+1 and finish tile k, and the PV
   // waves accumulate tile k-1; tile k + kAhead is issued in iteration k
   // into the buffer of tile k - 2 (finished at k - 2, accumulated at k - 1,
-  // so free after the barrier of iteration k).
+  // so free after the barrier of iteration k - 1).
   constexpr int kAhead = kNbuf - 2;
   // The QK look-ahead needs tile k+1 issued before iteration k, i.e. a ring of
   // at least 4 buffers (fp8 rows: 6; bf16 rows fit only 3 and run unpipelined,
   // tile k scored and finished in iteration k).
   constexpr bool kPipe = kNbuf >= 4;
-  // The first kAhead tiles go out at once (fp8 rows: 4; measured against 2,
-  // 3 and 5: with fewer, tile 2 is issued only when tiles 0 and 1 have landed
-  // and stalls iteration 1; with more, every workgroup's first tiles queue
-  // behind the others' later ones).  The rest follow one per iteration.
   const int npre = min(kAhead, ntiles);
-  auto src_of = [&](int tt) { return tile_src<FMT>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile, vwave, lane); };
-  auto issue = [&](int tt, const TileSrc<FMT>& src) {
-    issue_tile<FMT>(src, (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes), vwave, lane);
-  };
+  auto tile_lds = [&](int tt) { return (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes); };
   if (!qk_role)
-    for (int tt = 0; tt < npre; ++tt) issue(tt, src_of(tt));
+    for (int tt = 0; tt < npre; ++tt)
+      issue_tile<FMT, kInitIssuers>(
+          tile_src<FMT, kInitIssuers>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile, iw, lane), tile_lds(tt), iw,
+          lane);
 
-  // Top of iteration k: the PV waves wait for their share of the tile the QK
-  // waves start now, then a barrier publishes it (they issue more tiles later
-  // in the iteration).
+  // Top of iteration k (PV and loader waves): wait for this wave's share of
+  // the tile the QK waves start now; the barrier that follows publishes it.
+  // Loads complete in issue order, so the wait allows this wave's loads of
+  // every tile issued after it to stay in flight: its share of the later
+  // first-burst tiles, and (loader waves) of the later tiles issued so far
+  // (kAhead .. k - 1 + kAhead).
   auto wait_tile_loads = [&](int k) {
-    const int need = kPipe ? k + 1 : k;   // the tile the QK waves start in iteration k
-    const int issued = k == 0 ? npre : min(ntiles, k + kAhead);   // tiles issued so far
-    if (need < ntiles) {
-      const int after = issued - need - 1;                    // tiles issued after it
-      if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(after);
-      else wait_tiles<DmaCount<FMT>::kPoor>(after);
-    } else if (k < ntiles) {
-      if (vwave < DmaCount<FMT>::kRichWaves) wait_tiles<DmaCount<FMT>::of(0)>(0);
-      else wait_tiles<DmaCount<FMT>::kPoor>(0);
-    }
+    const int need = kPipe ? k + 1 : k;
+    if (need >= ntiles) return;
+    const int last = min(ntiles - 1, k - 1 + kAhead);            // last tile issued before this barrier
+    const int later = ld_role ? max(0, last - kAhead + 1) : 0;   // loader-issued tiles so far
+    if (need < npre)
+      wait_vmcnt_le<31>((npre - need - 1) * InitDma::per(iw) + later * LdDma::per(lw));
+    else if (ld_role)
+      wait_vmcnt_le<31>((last - need) * LdDma::per(lw));
   };
+  static_assert(3 * DmaCount<kFmtFp8, 8>::kPerWave + 2 * DmaCount<kFmtFp8, 4>::kPerWave <= 31 &&
+                3 * DmaCount<kFmtBf16, 8>::kPerWave <= 31, "vmcnt waits fit the dispatch range");
 
   if (qk_role) {
     // ---------------------------------------------------------------- QK role
-    // Raw Q of this wave's heads, loaded only now: its latency overlaps the
-    // first tiles' (issued by the PV waves after the barrier above) instead of
-    // delaying the index translation those tiles wait for.
-    const uint16_t* qrow = a.q + ((int64_t)vr * kHeads + head) * kDqk;
-    bf16x8 qraw[18];
-    if constexpr (FMT == kFmtFp8) {
-      // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
+    // Q of the group's 32 heads: 36,864 contiguous bytes, brought into ring
+    // buffer kAhead (first loaded with a tile only after the first loop
+    // barrier, by when Q has been read) with contiguous 1 KB direct-to-LDS
+    // loads, then read in the MFMA layout.  Loading it straight into the
+    // layout would touch ~32 cache lines per instruction, and the two token
+    // halves would load the same heads twice.
+    {
+      constexpr int kQBytes = kHpw * kDqk * 2;
+      static_assert(kQBytes % 1024 == 0 && (kNbuf - (kNbuf - 2)) * kTileBytes >= kQBytes, "Q fits the free buffers");
+      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)vr * kHeads + kHpw * hg) * kDqk);
+      uint8_t* qlds = tiles + (kNbuf - 2) * kTileBytes;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          qraw[4 * blk + j] = *reinterpret_cast<const bf16x8*>(qrow + 128 * blk + 32 * g + 8 * j);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 16; ++c)
-        qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+      for (int j = wave; j < kQBytes / 1024; j += kQkWaves)
+        dma16(qsrc + 1024 * j + 16 * lane, (uint32_t)(uintptr_t)(qlds + 1024 * j));
+      wait_vmcnt<0>();
     }
+    lds_barrier();   // the translation barrier (the other waves take it in their branch above); Q has landed
+    bf16x8 qraw[18];
+    {
+      const uint8_t* qrow = tiles + (kNbuf - 2) * kTileBytes + hloc * (kDqk * 2);
+      if constexpr (FMT == kFmtFp8) {
+        // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
 #pragma unroll
-    for (int c = 16; c < 18; ++c)
-      qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            qraw[4 * blk + j] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (128 * blk + 32 * g + 8 * j));
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (32 * c + 8 * g));
+      }
+#pragma unroll
+      for (int c = 16; c < 18; ++c)
+        qraw[c] = *reinterpret_cast<const bf16x8*>(qrow + 2 * (32 * c + 8 * g));
+    }
     i32x8 qhi[FMT == kFmtFp8 ? 4 : 1], qlo[FMT == kFmtFp8 ? 4 : 1];
     bf16x8 qb[18];
     float qscale = 1.0f;           // 2^-e_h, folded into the softmax scale
@@ -789,23 +827,38 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       lh_s[mh][hloc] = L;
     }
     lds_barrier();
+  } else if (ld_role) {
+    // ------------------------------------------------------------ loader role
+    // Tile k + kAhead goes out right after the barrier of iteration k; its
+    // sources are read from LDS a tile ahead.
+    TileSrc<FMT, kLdWaves> nsrc{};
+    if (kAhead < ntiles) nsrc = tile_src<FMT, kLdWaves>((const uint64_t LDS_AS*)rowaddr_s, kAhead * kTile, lw, lane);
+#pragma clang loop unroll(disable)
+    for (int k = 0; k <= ntiles; ++k) {
+      wait_tile_loads(k);
+      arrive_barrier();
+      if (k + kAhead < ntiles) {
+        issue_tile<FMT, kLdWaves>(nsrc, tile_lds(k + kAhead), lw, lane);
+        if (k + kAhead + 1 < ntiles)
+          nsrc = tile_src<FMT, kLdWaves>((const uint64_t LDS_AS*)rowaddr_s, (k + kAhead + 1) * kTile, lw, lane);
+      }
+    }
+    lds_barrier();                    // the QK waves publish each half's max and sum
   } else {
     // ---------------------------------------------------------------- PV role
     // 32x32x16 bf16 MFMA: O^T[32 d][32 heads] += V^T[32 d][16 tok] . P^T[16 tok][32 heads],
     // one accumulator per 16-token half (each half has its own running max).
     // Operand lane layout (both): row/col = lane % 32, k = 8 * (lane / 32) + i,
     // so k-slot (lane/32, i) of half kh is token 16kh + 8(lane/32) + i.
-    const int pw = wave - kQkWaves;   // PV wave 0 .. 7
-    const int vb = pw >> 1;           // scale block (128-dim slice of the latent) ...
-    const int dh = pw & 1;            // ... and which 64-dim half of it this wave owns
+    const int vb = wave - kQkWaves;   // scale block / 128-dim slice of the latent
     const int l32 = lane & 31, kg = lane >> 5;
-    f32x16 o[2][2];                   // [32-dim block of the half-slice][token half]
+    f32x16 o[4][2];                   // [32-dim block of the slice][token half]
     // zero from an asm statement, so the compiler cannot hoist the zeroing
     // above the role branch and keep 128 registers live through the QK path
     float zero;
     asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) o[i][j] = zero;
 
@@ -814,25 +867,24 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // MFMAs of tile k-1), so their latency hides under the MFMAs and the
     // barrier.  Tile k is published by the barrier of iteration k - 1 (k when
     // unpipelined) and its buffer is reloaded only in iteration k + 2.
-    typename VRaw<FMT>::type vnext[2][2];
+    typename VRaw<FMT>::type vnext[2][4];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int dl = 0; dl < 2; ++dl) vnext[kh][dl] = {};
+      for (int db = 0; db < 4; ++db) vnext[kh][db] = {};
     auto read_v = [&](int kt) {
       const uint8_t* tb = tiles + (kt % kNbuf) * kTileBytes;
       const int gg = lane >> 4;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int dl = 0; dl < 2; ++dl) {
-          const int db = 2 * dh + dl;   // 32-dim block within the scale block
+        for (int db = 0; db < 4; ++db) {
           if constexpr (FMT == kFmtFp8) {
             // 16-lane group gg reads tokens 16kh + 8(gg>>1) + 0..7 x dims
             // 32db + 16(gg&1) + 0..15; source lane (2r + half) supplies 8 bytes of row r
             const int r = c16 >> 1, half = c16 & 1;
             const uint8_t* src = tb + TL::off(16 * kh + 8 * (gg >> 1) + r, 8 * vb + 2 * db + (gg & 1)) + 8 * half;
-            vnext[kh][dl] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
+            vnext[kh][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS_AS*)src);
           } else {
             // two 4-row reads per group: rows 16kh + 8(gg>>1) + 0..3 and + 4..7;
             // source lane (4r + q) supplies 4 elements of row r
@@ -846,12 +898,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
             // result were mis-lowered (the upper dword was dropped)
             const i32x2 a0 = __builtin_bit_cast(i32x2, r0);
             const i32x2 a1 = __builtin_bit_cast(i32x2, r1);
-            vnext[kh][dl] = i32x4{a0[0], a0[1], a1[0], a1[1]};
+            vnext[kh][db] = i32x4{a0[0], a0[1], a1[0], a1[1]};
           }
         }
     };
 
-    TileSrc<FMT> nsrc{};              // load sources of the next tile to issue
     // Iteration 0 has no P yet: it is a warm-up pass through the same loop
     // code on zero operands and an unwritten P buffer (loading the
     // instructions into the cache while the QK waves score tile 0); its
@@ -878,44 +929,31 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       for (int kh = 0; kh < 2; ++kh)
         if (__builtin_amdgcn_ballot_w64(al[kh] != 1.0f)) {
 #pragma unroll
-          for (int dl = 0; dl < 2; ++dl) o[dl][kh] *= al[kh];
+          for (int db = 0; db < 4; ++db) o[db][kh] *= al[kh];
         }
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-        for (int dl = 0; dl < 2; ++dl) {
+        for (int db = 0; db < 4; ++db) {
           bf16x8 va;
           if constexpr (FMT == kFmtFp8) {
-            const i32x2 raw = vnext[kh][dl];
+            const i32x2 raw = vnext[kh][db];
             va = fp8x8_to_bf16((uint64_t)(uint32_t)raw[0] | ((uint64_t)(uint32_t)raw[1] << 32));
           } else {
-            va = __builtin_bit_cast(bf16x8, vnext[kh][dl]);
+            va = __builtin_bit_cast(bf16x8, vnext[kh][db]);
           }
-          o[dl][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[kh], o[dl][kh], 0, 0, 0);
+          o[db][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pv[kh], o[db][kh], 0, 0, 0);
         }
+      }
       if (dry) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
       }
-      // V^T of tile k first, so the reads' latency runs under the load issue
-      // below rather than ahead of the next barrier.
+      // V^T of tile k, read one iteration ahead: the reads' latency runs under
+      // the barrier and the next P reads.
       if (k < ntiles) read_v(k);
-      // Tile k + kAhead goes out after this iteration's MFMAs: each 1 KB
-      // direct-to-LDS instruction is slow to leave the issue queue, and the
-      // MFMAs run meanwhile.  Its buffer held tile k - 2, done with by every
-      // wave before this iteration's barrier.
-      // The next tile's sources are read a tile ahead (fp8 rows: 6 registers;
-      // bf16 rows: 10) so the loads go out without waiting on LDS.
-      constexpr bool kSrcAhead = true;
-      if (k == 0) {
-        for (int tt = npre; tt <= kAhead && tt < ntiles; ++tt) issue(tt, src_of(tt));
-        if (kSrcAhead && kAhead + 1 < ntiles) nsrc = src_of(kAhead + 1);
-      } else if (k + kAhead < ntiles) {
-        issue(k + kAhead, kSrcAhead ? nsrc : src_of(k + kAhead));
-        if (kSrcAhead && k + kAhead + 1 < ntiles) nsrc = src_of(k + kAhead + 1);
-      }
     }
 
     lds_barrier();                    // QK waves have published each half's max and sum
@@ -935,33 +973,33 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       lse_v = Lh > 0.f ? (M + __builtin_amdgcn_logf(Lh)) * kLn2 : -INFINITY;
     }
     const int ghead = kHpw * hg + l32;
-    if (pw == 0 && kg == 0) {
+    if (vb == 0 && kg == 0) {
       lsev_s[l32] = lse_v;
       if (a.nsplit == 1) a.lse[(int64_t)vr * kHeads + ghead] = lse_v;
       else if (!(fused && last_s)) store_agent(a.part_lse + ((int64_t)vr * a.nsplit + s) * kHeads + ghead, lse_v);
     }
-    // register j of o[dl][*] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head l32], db = 2dh + dl
-    f32x16 res[2];
+    // register j of o[db][*] holds O^T[d = 128vb + 32db + 8(j/4) + 4kg + j%4][head l32]
+    f32x16 res[4];
 #pragma unroll
-    for (int dl = 0; dl < 2; ++dl) res[dl] = o[dl][0] * f[0] + o[dl][1] * f[1];
+    for (int db = 0; db < 4; ++db) res[db] = o[db][0] * f[0] + o[db][1] * f[1];
     if (a.nsplit == 1) {
       uint16_t* orow = a.out + ((int64_t)vr * kHeads + ghead) * kDv + 128 * vb + 4 * kg;
 #pragma unroll
-      for (int dl = 0; dl < 2; ++dl)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[dl][4 * jj]) | ((uint32_t)f32_to_bf16_rne(res[dl][4 * jj + 1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[dl][4 * jj + 2]) | ((uint32_t)f32_to_bf16_rne(res[dl][4 * jj + 3]) << 16);
-          *reinterpret_cast<uint2*>(orow + 32 * (2 * dh + dl) + 8 * jj) = make_uint2(lo, hi);
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[db][4 * jj]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[db][4 * jj + 2]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 3]) << 16);
+          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
         }
     } else if (!fused || !last_s) {
       const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)vr * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
-      for (int dl = 0; dl < 2; ++dl)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 v = {res[dl][4 * jj], res[dl][4 * jj + 1], res[dl][4 * jj + 2], res[dl][4 * jj + 3]};
-          const uint32_t off = part_run_offset(vb, 2 * dh + dl, jj, hg, lane);
+          const f32x4 v = {res[db][4 * jj], res[db][4 * jj + 1], res[db][4 * jj + 2], res[db][4 * jj + 3]};
+          const uint32_t off = part_run_offset(vb, db, jj, hg, lane);
           if (fused)   // read back in this launch, possibly on another XCD
             __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSc1);
           else         // read by the combine launch
@@ -971,11 +1009,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       // last split of this (request, head group): its own partial goes to
       // LDS, at the offsets it has in a workspace block
 #pragma unroll
-      for (int dl = 0; dl < 2; ++dl)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, 2 * dh + dl, jj, hg, lane)) =
-              f32x4{res[dl][4 * jj], res[dl][4 * jj + 1], res[dl][4 * jj + 2], res[dl][4 * jj + 3]};
+          *reinterpret_cast<f32x4*>(smem + part_run_offset(vb, db, jj, hg, lane)) =
+              f32x4{res[db][4 * jj], res[db][4 * jj + 1], res[db][4 * jj + 2], res[db][4 * jj + 3]};
     }
   }
 

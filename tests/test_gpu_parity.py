@@ -369,3 +369,54 @@ def test_query_sets_beyond_the_in_kernel_merge_limit():
     with pytest.raises(smla.SmlaError):
         smla.plan_for(shape, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL})
     _check(w, plan={"nsplit": 2}, what="4120 query sets, nsplit 2")
+
+
+# --------------------------------------------------------------- a dominant token: live rescale and lse spread
+def _dominant_workload(fmt, shared=1.5, seed=960):
+    """Three requests in which the token at top-k slot 300 + 17b (tile 9 or 10 of
+    16) scores about 30 nats above every other selected token, for every head:
+    all heads' q share a component `shared * u` on the 512 latent dims (u a
+    fixed +-1 pattern) and that token's latent is u with zero rope.  Unsplit,
+    the running maximum then jumps after nine tiles have been accumulated (the
+    rescale of live accumulators); split, one split's lse lies ~25 nats above
+    the others'.  Rows and Q are built here from the generator's own encoders."""
+    B = 3
+    w = W.build("dominant", seed, fmt, B, [8192, 20000, 4096], fmt, "uniform")
+    rng = np.random.default_rng(seed)
+    u = rng.choice([-1.0, 1.0], size=W.D_LATENT).astype(np.float32)
+    qf = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).float().numpy()
+    qf[:, :, :W.D_LATENT] += np.float32(shared) * u
+    w.q = W.bf16_bits(qf)
+    planted = W.pack_rows(fmt, u[None, :], np.zeros((1, W.D_ROPE), np.float32))[0]
+    slots = []
+    for b in range(B):
+        i = int(w.topk_idx[b, 300 + 17 * b])
+        slot = int(w.page_table[b, i // W.PAGE]) * W.PAGE + i % W.PAGE
+        k = int(np.searchsorted(w.row_slots, slot))
+        assert w.row_slots[k] == slot
+        w.row_data[k] = planted
+        slots.append(slot)
+    return w
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
+def test_dominant_late_token_rescales_live_accumulators(fmt):
+    """Unsplit (nsplit = 1) and one tile per split (nsplit = 16): the oracle's
+    lse sits ~30 nats up, set by the planted token, and the kernel must match."""
+    w = _dominant_workload(fmt)
+    ref_o, ref_l = oracle.decode_workload(w)
+    assert ref_l.min() > 20.0, ref_l.min()          # the planted token dominates every head
+    for ns in (1, 16):
+        _check(w, plan={"nsplit": ns, "merge": smla.MERGE_IN_KERNEL if ns > 1 else smla.MERGE_AUTO},
+               what=f"dominant late token nsplit={ns} fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
+def test_merge_of_splits_with_far_apart_lse(fmt):
+    """The dominant token sits in one split, so that split's lse is ~25 nats above
+    the others' and their weights underflow to ~1e-11: both merge placements and
+    the two-stage form must give the oracle's result (and each other's bits)."""
+    w = _dominant_workload(fmt)
+    for ns in (2, 4, 16):
+        for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+            _check(w, plan={"nsplit": ns, "merge": merge}, what=f"far-apart lse nsplit={ns} merge={merge} fmt={fmt}")
