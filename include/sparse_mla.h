@@ -181,6 +181,31 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sparse_mla_decode_noalloc -- sparse_mla_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, plans, kernels and results
+ * (bit for bit) as sparse_mla_decode, without the workspace arguments: the
+ * workspace is a device array that the library holds,
+ * SMLA_NOALLOC_SCRATCH_BYTES per GPU, from the library's load on that GPU
+ * until the process ends.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library routine.
+ *   - Returns SMLA_ERR_WORKSPACE, launching nothing, when the plan needs more
+ *     workspace than that (smla_plan_for's workspace_bytes; each split
+ *     partial takes 128 KiB + 256 B per (request, query token, split), plus
+ *     the 64 KiB counter head), e.g. B * q_len * nsplit above ~250.
+ *   - The first call on a GPU that needs the array looks up its device
+ *     address and zeroes its counter head with a fill kernel on `stream`.
+ *   - Every call on one GPU uses that GPU's one array, and a call leaves it
+ *     holding its partials: calls that overlap in time on one GPU (different
+ *     streams or threads) race and must be serialised by the caller.
+ * Returns as sparse_mla_decode does.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int sparse_mla_decode_noalloc(const void* q, const void* kv_pool, const int32_t* page_table,
+                              const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
+                              float* lse, const smla_shape* shape, const smla_plan* plan_or_null, void* stream);
+
+/*
  * smla_decode_split / smla_decode_combine -- the two stages of
  * sparse_mla_decode as separate calls (a split kernel per (request, top-k
  * split), then the log-sum-exp combine kernel), for callers that schedule or

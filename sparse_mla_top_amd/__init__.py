@@ -31,6 +31,7 @@ ERR_WORKSPACE = -3
 ERR_PLAN = -4
 ERR_HIP = -5
 ERR_INDEX = -6       # validate mode (environment SMLA_VALIDATE=1): an index or page id out of range
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the workspace that sparse_mla_decode_noalloc brings, per GPU
 
 MERGE_AUTO = 0
 MERGE_IN_KERNEL = 1
@@ -78,6 +79,9 @@ def lib():
         L.sparse_mla_decode.argtypes = [vp, vp, i32p, i32p, i32p, ctypes.c_float, vp, vp,
                                         ctypes.POINTER(Shape), ctypes.POINTER(Plan), vp, ctypes.c_size_t, vp]
         L.sparse_mla_decode.restype = ctypes.c_int
+        L.sparse_mla_decode_noalloc.argtypes = [vp, vp, i32p, i32p, i32p, ctypes.c_float, vp, vp,
+                                                ctypes.POINTER(Shape), ctypes.POINTER(Plan), vp]
+        L.sparse_mla_decode_noalloc.restype = ctypes.c_int
         L.smla_decode_split.argtypes = L.sparse_mla_decode.argtypes
         L.smla_decode_split.restype = ctypes.c_int
         L.smla_decode_combine.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Plan), vp, ctypes.c_size_t, vp, vp, vp]
@@ -178,6 +182,16 @@ def decode_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape
     return lib().sparse_mla_decode(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
                                    float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape), _plan_arg(plan),
                                    _ptr(workspace), ctypes.c_size_t(ws_bytes), _stream(stream))
+
+
+def decode_noalloc_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape: Shape, plan=None,
+                       stream=None) -> int:
+    """sparse_mla_decode_noalloc on torch tensors (the workspace is the library's
+    own device array); returns the library's status code."""
+    _check_tensors(shape, q, kv_pool, page_table, topk_idx, ctx_len, out, lse)
+    return lib().sparse_mla_decode_noalloc(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(topk_idx), _ptr(ctx_len),
+                                           float(scale), _ptr(out), _ptr(lse), ctypes.byref(shape), _plan_arg(plan),
+                                           _stream(stream))
 
 
 def split_raw(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape: Shape, plan=None,

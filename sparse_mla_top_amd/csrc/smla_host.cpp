@@ -277,6 +277,20 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
                       const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
                       float* lse, const smla_shape* shape, const smla_plan* plan_or_null,
                       void* workspace, size_t workspace_bytes, void* stream) {
+  return smla::decode_with_workspace(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
+                                     workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+size_t smla::workspace_counter_bytes() { return kCounterBytes; }
+
+// The body of sparse_mla_decode, shared with the entry point that brings its
+// own workspace (smla_noalloc.hip).
+int smla::decode_with_workspace(const void* q, const void* kv_pool, const int32_t* page_table,
+                                const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,
+                                float* lse, const smla_shape* shape, const smla_plan* plan_or_null,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pr;
   int rc = prepare(q, kv_pool, page_table, topk_idx, ctx_len, scale, out, lse, shape, plan_or_null,
                    workspace, workspace_bytes, &pr);
@@ -293,6 +307,8 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
   if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   return SMLA_OK;
 }
+
+extern "C" {
 
 int smla_decode_split(const void* q, const void* kv_pool, const int32_t* page_table,
                       const int32_t* topk_idx, const int32_t* ctx_len, float scale, void* out,

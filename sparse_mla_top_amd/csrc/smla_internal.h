@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/sparse_mla.h"
+
 namespace smla {
 
 constexpr int kHeads = 64;
@@ -71,5 +73,13 @@ hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t st
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int fmt, int B, hipStream_t stream);
 hipError_t launch_zero(uint32_t* p, size_t n, hipStream_t stream);
+
+// sparse_mla_decode with a given workspace (defined in smla_host.cpp; the C
+// entry points sparse_mla_decode and sparse_mla_decode_noalloc call it).
+int decode_with_workspace(const void* q, const void* kv_pool, const int32_t* page_table, const int32_t* topk_idx,
+                          const int32_t* ctx_len, float scale, void* out, float* lse, const smla_shape* shape,
+                          const smla_plan* plan_or_null, void* workspace, size_t workspace_bytes, void* stream);
+// Bytes of the fixed counter head at the start of every workspace.
+size_t workspace_counter_bytes();
 
 }  // namespace smla
