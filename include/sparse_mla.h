@@ -85,6 +85,9 @@ typedef enum {
 #define SMLA_ERR_INDEX (-6)             /* validate mode only: a top-k index other than -1  */
                                         /* outside [0, ctx_len), past the page-table row,   */
                                         /* or on a page id outside [0, pool_pages)          */
+#define SMLA_ERR_MERGE (-7)             /* validate mode only: an in-kernel split merge gave */
+                                        /* up waiting (workspace status word set; see       */
+                                        /* sparse_mla_decode): smla_workspace_init needed   */
 
 typedef struct {
     int32_t batch;             /* B >= 0 requests                                   */
@@ -158,14 +161,29 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *   shape      [host]   problem description
  *   plan_or_null [host] NULL = automatic plan; else as for smla_plan_for's override
  *   workspace  [device] scratch of at least the size smla_plan_for reports
- *                        (may be NULL when that size is 0).  Its first 64 KiB hold
- *                        the arrival counters of the in-kernel merge, at the same
- *                        place for every shape and plan; the split partials follow.
- *                        It must be zero-filled once before its first use
- *                        (smla_workspace_init); every successful call leaves the
- *                        counters at zero again, so one workspace serves calls of
- *                        any batch size and split count that fit in it.
- *                        Calls that share a workspace must not overlap in time.
+ *                        (may be NULL when that size is 0).  Its first 64 KiB +
+ *                        256 B hold the arrival counters of the in-kernel merge
+ *                        and a status word, at the same place for every shape and
+ *                        plan; the split partials follow.  It must be zero-filled
+ *                        once before its first use (smla_workspace_init); every
+ *                        successful call leaves the counters at zero again, so one
+ *                        workspace serves calls of any batch size and split count
+ *                        that fit in it.  Calls that share a workspace must not
+ *                        overlap in time.
+ *                        The in-kernel merge waits a bounded time for the other
+ *                        splits of its request (they are resident and past their
+ *                        compute, so the bound is only reached when something
+ *                        went wrong).  If it gives up, it sets the status word,
+ *                        leaves the counters as they are, still merges what the
+ *                        partials hold and writes NaN into lse for that request's
+ *                        heads; while the status word is set every call that
+ *                        merges in-kernel on the workspace writes NaN into lse and
+ *                        leaves out as it was.  A NaN lse therefore
+ *                        means: call smla_workspace_init before the workspace's
+ *                        next use.  In validate mode the call waits and returns
+ *                        SMLA_ERR_MERGE when the status word is set.  (The
+ *                        environment variable SMLA_MERGE_SPIN_LIMIT, read at every
+ *                        call, lowers the bound: tests use it to drive this path.)
  *   stream     hipStream_t (NULL = default stream)
  * With nsplit = 1 the work is one kernel launch.  Otherwise each (request,
  * split) workgroup writes its partial result and the partials are merged by
@@ -194,7 +212,10 @@ int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_ta
  *     partial takes 128 KiB + 256 B per (request, query token, split), plus
  *     the 64 KiB counter head), e.g. B * q_len * nsplit above ~250.
  *   - The first call on a GPU that needs the array looks up its device
- *     address and zeroes its counter head with a fill kernel on `stream`.
+ *     address and zeroes its counter head and status word with a fill kernel
+ *     on `stream`.  A merge that gave up (see sparse_mla_decode) leaves that
+ *     GPU's array marked for the rest of the process: lse then comes out NaN
+ *     on every in-kernel merge.
  *   - Every call on one GPU uses that GPU's one array, and a call leaves it
  *     holding its partials: calls that overlap in time on one GPU (different
  *     streams or threads) race and must be serialised by the caller.
@@ -296,9 +317,11 @@ int smla_indexer_topk(const void* q_idx, const float* head_w, const void* key_po
                       void* stream);
 
 /*
- * smla_workspace_init -- zero a workspace (its arrival counters) on `stream`
- * with a fill kernel, before its first use by sparse_mla_decode, or after a
- * call that did not complete.  workspace [device], 4-byte aligned.
+ * smla_workspace_init -- zero a workspace (its arrival counters and status
+ * word) on `stream` with a fill kernel, before its first use by
+ * sparse_mla_decode, after a call that did not complete, or after a merge gave
+ * up waiting (NaN lse, or SMLA_ERR_MERGE in validate mode).
+ * workspace [device], 4-byte aligned.
  */
 int smla_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 

@@ -31,6 +31,7 @@ ERR_WORKSPACE = -3
 ERR_PLAN = -4
 ERR_HIP = -5
 ERR_INDEX = -6       # validate mode (environment SMLA_VALIDATE=1): an index or page id out of range
+ERR_MERGE = -7       # validate mode: an in-kernel split merge gave up waiting (smla_workspace_init needed)
 NOALLOC_SCRATCH_BYTES = 32 << 20   # the workspace that sparse_mla_decode_noalloc brings, per GPU
 
 MERGE_AUTO = 0

@@ -60,15 +60,19 @@ int query_sets(const smla_shape* s) { return s->batch * q_len_of(s); }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout (nsplit > 1), per query set (request, query token), Q sets
-// in all: a fixed 64 KiB head of uint32 arrival counters [Q][head group][2]
-// (tickets, finished partial writes; room for kMaxMergeSets sets), then fp32
-// partial outputs [Q, nsplit, 64, 512] and fp32 partial lse [Q, nsplit, 64],
-// each region at a 256-byte boundary.  The counters sit at the same place for
-// every shape and plan, and partial writes never reach them, so a workspace
-// reused across batch sizes and split counts finds them at zero (each call
-// that merges in-kernel resets its own).
+// in all: a fixed head of 64 KiB of uint32 arrival counters [Q][head group][2]
+// (tickets, finished partial writes; room for kMaxMergeSets sets) and a
+// 256-byte block holding the status word, then fp32 partial outputs
+// [Q, nsplit, 64, 512] and fp32 partial lse [Q, nsplit, 64], each region at a
+// 256-byte boundary.  The head sits at the same place for every shape and
+// plan, and partial writes never reach it, so a workspace reused across batch
+// sizes and split counts finds the counters at zero (each call that merges
+// in-kernel resets its own).  The status word is non-zero once a merge has
+// given up waiting (its counters may then be off); only smla_workspace_init
+// clears it.
 constexpr int kMaxMergeSets = 4096;
-constexpr size_t kCounterBytes = (size_t)kMaxMergeSets * kHeadGroups * 2 * sizeof(uint32_t);
+constexpr size_t kCountersOnly = (size_t)kMaxMergeSets * kHeadGroups * 2 * sizeof(uint32_t);
+constexpr size_t kCounterBytes = kCountersOnly + 256;   // counters + status block
 static_assert(kCounterBytes % 256 == 0, "counter head keeps the partials 256-byte aligned");
 size_t ws_part_o_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * kDv * sizeof(float)); }
 size_t ws_part_lse_bytes(int B, int nsplit) { return align256((size_t)B * nsplit * kHeads * sizeof(float)); }
@@ -135,6 +139,7 @@ const char* smla_strerror(int code) {
     case SMLA_ERR_PLAN: return "plan override outside the supported values";
     case SMLA_ERR_HIP: return "HIP runtime error";
     case SMLA_ERR_INDEX: return "a top-k index or page id outside its range (validate mode)";
+    case SMLA_ERR_MERGE: return "a split merge gave up waiting; the workspace needs smla_workspace_init (validate mode)";
     default: return "unknown error";
   }
 }
@@ -193,6 +198,21 @@ int smla_plan_for(const smla_shape* shape, const smla_plan* ov, smla_plan* out, 
   return smla_plan_for_cus(shape, ov, cus, out, workspace_bytes);
 }
 
+// Polls a merging workgroup makes before it gives up.  The environment
+// variable SMLA_MERGE_SPIN_LIMIT (read at every call) lowers it, so tests can
+// drive the give-up path with every kernel still running to completion.
+static int merge_spin_limit() {
+  const char* v = std::getenv("SMLA_MERGE_SPIN_LIMIT");
+  if (!v || !*v) return kMergeSpinLimit;
+  const long n = std::strtol(v, nullptr, 10);
+  return n < 0 ? 0 : (n > kMergeSpinLimit ? kMergeSpinLimit : (int)n);
+}
+
+static bool validate_mode() {
+  const char* v = std::getenv("SMLA_VALIDATE");
+  return v && v[0] == '1';
+}
+
 // Validate mode (environment SMLA_VALIDATE=1, read at every call): before any
 // launch, check the top-k indices and page ids and fail with SMLA_ERR_INDEX
 // where the kernels would mask a slot for a reason other than a -1 entry.
@@ -200,8 +220,7 @@ int smla_plan_for(const smla_shape* shape, const smla_plan* ov, smla_plan* out, 
 // debugging, not for graph capture.
 static int check_indices(const int32_t* page_table, const int32_t* topk_idx, const int32_t* ctx_len,
                          const smla_shape* shape, void* stream) {
-  const char* v = std::getenv("SMLA_VALIDATE");
-  if (!v || v[0] != '1' || shape->batch == 0) return SMLA_OK;
+  if (!validate_mode() || shape->batch == 0) return SMLA_OK;
   unsigned bad = 0;
   if (launch_validate(page_table, topk_idx, ctx_len, shape->batch, shape->max_pages_per_req, shape->pool_pages,
                       (hipStream_t)stream, &bad) != hipSuccess)
@@ -254,8 +273,11 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   a.part_o = nullptr;
   a.part_lse = nullptr;
   a.counters = nullptr;
+  a.status = nullptr;
+  a.spin_limit = merge_spin_limit();
   if (plan.nsplit > 1) {
     a.counters = (uint32_t*)workspace;
+    a.status = (uint32_t*)((uint8_t*)workspace + kCountersOnly);
     a.part_o = (float*)((uint8_t*)workspace + kCounterBytes);
     a.part_lse = (float*)((uint8_t*)workspace + kCounterBytes + ws_part_o_bytes(Q, plan.nsplit));
   }
@@ -305,6 +327,14 @@ int smla::decode_with_workspace(const void* q, const void* kv_pool, const int32_
   }
   // one launch: the last split of each request merges the partials
   if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
+  // validate mode: wait, and report a merge that gave up (the workspace status word)
+  if (pr.nsplit > 1 && validate_mode()) {
+    uint32_t st = 0;
+    if (hipMemcpyAsync(&st, pr.split.status, sizeof st, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+        hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+      return SMLA_ERR_HIP;
+    if (st) return SMLA_ERR_MERGE;
+  }
   return SMLA_OK;
 }
 

@@ -29,6 +29,7 @@ constexpr int kRowBytesBf16 = 2 * kDqk;                  // 1152
 constexpr int kRowBytesFp8 = kDl + 16 + 2 * 64;          // 656
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
+constexpr int kMergeSpinLimit = 1 << 22;   // polls before a merging workgroup gives up
 
 struct SplitArgs {
   const uint16_t* q;           // bf16 [B][q_len][64][576]
@@ -48,6 +49,8 @@ struct SplitArgs {
   uint16_t* out;               // bf16 [qs][64][512] (written directly when nsplit == 1)
   float* lse;                  // [qs][64]
   uint32_t* counters;          // [qs][head group][2] tickets / finished writes; non-null: the last split merges
+  uint32_t* status;            // workspace status word (non-zero: a merge gave up waiting; see sparse_mla.h)
+  int spin_limit;              // polls before a merging workgroup gives up
 };
 
 struct CombineArgs {

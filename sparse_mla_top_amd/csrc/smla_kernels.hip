@@ -261,7 +261,8 @@ __device__ __forceinline__ uint32_t part_run_offset(int vb, int db, int jj, int 
 constexpr uint32_t kPartBytes = kHeads * kDv * 4;
 // Polls of the finished-writes counter before a merging workgroup gives up
 // (never reached when every split runs: they are all past their compute).
-constexpr int kSpinLimit = 1 << 22;
+// The launch passes the limit (SplitArgs::spin_limit, at most kMergeSpinLimit):
+// tests force the give-up path with a limit of 0.
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
@@ -447,6 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   __shared__ float alpha_s[2][2][kHpw];            // [buffer][half][head]
   __shared__ float mh_s[2][kHpw], lh_s[2][kHpw];   // per half: running max (log2) and sum
   __shared__ int last_s;
+  __shared__ int poison_s;                         // the workspace status word was set before this call
   __shared__ float lsev_s[kHpw];                   // this split's lse per head
   __shared__ int fail_s;
 
@@ -540,9 +542,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // every tile issued after it to stay in flight: its share of the later
   // first-burst tiles, and (loader waves) of the later tiles issued so far
   // (kAhead .. k - 1 + kAhead).
+  // Iteration 0 of the pipelined loop reads tiles 0 and 1, so a split of one
+  // tile still waits for tile 0 there.
   auto wait_tile_loads = [&](int k) {
-    const int need = kPipe ? k + 1 : k;
-    if (need >= ntiles) return;
+    int need = kPipe ? k + 1 : k;
+    if (need >= ntiles) {
+      if (!(kPipe && k == 0)) return;
+      need = ntiles - 1;
+    }
     const int last = min(ntiles - 1, k - 1 + kAhead);            // last tile issued before this barrier
     const int later = ld_role ? max(0, last - kAhead + 1) : 0;   // loader-issued tiles so far
     if (need < npre)
@@ -817,9 +824,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // which waits on nothing): take the arrival ticket of this (request, head
     // group) now, so its latency overlaps that tile.  The holder of the last
     // ticket merges.
-    if (fused && threadIdx.x == 0)
+    if (fused && threadIdx.x == 0) {
       last_s = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                (uint32_t)(a.nsplit - 1);
+      poison_s = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    }
     // this half's max and sum of each head for the PV waves
     const float L = wave_sum16(l_run);
     if (g == 0) {
@@ -1019,6 +1028,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 
   // ---- fused merge
   if (!fused) return;
+  if (poison_s) {
+    // An earlier merge on this workspace gave up and left its counters off, so
+    // no split can tell whether it is the last: lse is NaN (out is left as
+    // is) until smla_workspace_init clears the workspace.
+    if (threadIdx.x < kHpw) a.lse[(int64_t)vr * kHeads + kHpw * hg + threadIdx.x] = __builtin_nanf("");
+    return;
+  }
   if (!last_s) {
     wait_stores();                       // this wave's partial stores have completed ...
     lds_barrier();                       // ... and so have every other wave's
@@ -1029,14 +1045,20 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // past their compute) have finished writing, then merge with all 8 waves,
   // this split's own partial and lse read from LDS.
   if (threadIdx.x == 0) {
-    bool ok = false;
-    for (int it = 0; it < kSpinLimit && !ok; ++it) {
-      ok = __hip_atomic_load(&ctr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(a.nsplit - 1);
-      if (!ok) __builtin_amdgcn_s_sleep(2);
+    bool done = false;
+    for (int it = 0; it < a.spin_limit && !done; ++it) {
+      done = __hip_atomic_load(&ctr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)(a.nsplit - 1);
+      if (!done) __builtin_amdgcn_s_sleep(2);
     }
-    fail_s = ok ? 0 : 1;
-    ctr[0] = 0u;                         // both counters back to zero for the next call
-    ctr[1] = 0u;
+    if (done) {
+      ctr[0] = 0u;                       // both counters back to zero for the next call
+      ctr[1] = 0u;
+    } else {
+      // gave up: the counters stay as they are (a straggler may still add to
+      // them) and the status word marks the workspace for later calls
+      __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    fail_s = done ? 0 : 1;
   }
   lds_barrier();
   merge_fused(a.part_o, a.part_lse, a.nsplit, vr, hg, s, smem, lsev_s, a.out, a.lse,

@@ -35,10 +35,10 @@ def test_version_and_row_bytes():
     assert L.smla_row_bytes(smla.KV_BF16) == 1152
     assert L.smla_row_bytes(smla.KV_FP8) == 656
     assert L.smla_row_bytes(7) == -1
-    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert smla.strerror(code)
     # every error code has its own message, and the binding's constants are the header's
-    assert len({smla.strerror(c) for c in (-1, -2, -3, -4, -5, -6)}) == 6
+    assert len({smla.strerror(c) for c in (-1, -2, -3, -4, -5, -6, -7)}) == 7
     hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "sparse_mla.h")).read()
     for name in ("INVALID_ARG", "UNSUPPORTED_SHAPE", "WORKSPACE", "PLAN", "HIP", "INDEX"):
         m = re.search(r"#define SMLA_ERR_%s \((-\d+)\)" % name, hdr)
@@ -95,8 +95,9 @@ def test_forced_nsplit_normalised_to_whole_tiles(forced, expect):
     chunk = math.ceil(16 / p.nsplit)
     assert (p.nsplit - 1) * chunk < 16 <= p.nsplit * chunk
     a256 = lambda x: (x + 255) // 256 * 256
-    # a fixed 64 KiB head of arrival counters, then partial outputs and partial lse
-    assert ws == (0 if expect == 1 else 65536 + a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4))
+    # a fixed head (64 KiB of arrival counters, a 256-byte status block), then
+    # partial outputs and partial lse
+    assert ws == (0 if expect == 1 else 65536 + 256 + a256(8 * expect * 64 * 512 * 4) + a256(8 * expect * 64 * 4))
 
 
 def test_selector_is_shape_only_and_bounded():
@@ -173,7 +174,7 @@ def test_query_tokens_scale_the_workspace_and_grid():
         a256 = lambda x: (x + 255) // 256 * 256
         for q in (1, 2, 3, 4):
             Q = 6 * q
-            assert ws[q] == 65536 + a256(Q * ns * 64 * 512 * 4) + a256(Q * ns * 64 * 4)
+            assert ws[q] == 65536 + 256 + a256(Q * ns * 64 * 512 * 4) + a256(Q * ns * 64 * 4)
     # more query tokens never ask for more splits (the grid already fills more of the device)
     for B in (1, 4, 16, 32):
         picks = [smla.plan_for_cus(_shape(batch=B, q_len=q), 256)[0].nsplit for q in (1, 2, 3, 4)]

@@ -88,6 +88,16 @@ def test_decode_forced_nsplit(nsplit, fmt):
         _check(w, plan={"nsplit": nsplit, "merge": merge}, what=f"forced nsplit={nsplit} merge={merge} fmt={fmt}")
 
 
+@pytest.mark.parametrize("nsplit", [6, 16])
+def test_one_tile_splits_under_load(nsplit):
+    """Splits holding a single 32-token tile (all of them at 16 splits, the
+    last one at 6) read that tile in their first iteration: at B = 96 the row
+    loads are slow enough that a missing wait for them shows."""
+    w = W.make(4)
+    for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+        _check(w, plan={"nsplit": nsplit, "merge": merge}, what=f"one-tile splits nsplit={nsplit} merge={merge}")
+
+
 def test_nsplit_results_agree():
     w = W.build("agree", 931, 0, 5, [65536, 4096, 700, 300, 131072], W.FMT_FP8, "uniform")
     d = upload(w)
