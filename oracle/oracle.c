@@ -31,7 +31,7 @@
  *     out[h][d]    =  sum_t w_t * v[t][d] / L,   lse[h] = m + ln L
  *     no valid slot:  out[h][:] = 0,  lse[h] = -inf
  *
- * Readings where the pages are silent (each listed in the design notes):
+ * Readings where the pages are silent:
  *   - K = [latent; rope] (576 dims) and V = latent (512 dims): absorbed MLA decode.
  *   - Row formats: fp8 = 512 e4m3 codes | 4 little-endian fp32 scales (scale j
  *     covers dims 128j..128j+127) | 64 bf16 rope values (656 B);
@@ -244,10 +244,9 @@ int oracle_decode(int B, int H, int topk, int max_pages, int64_t pool_pages, int
 
 /* ---- the cache producer: quantise and write new tokens' rows -------------
  *
- * The row format above, written from fp32 values (§8(f) rank 2 of the build
- * notes; the pages name the FP8 latent cache and a fused epilogue that would
- * produce it: "Inside the Decode Performance Investigation", sections "Task 1"
- * and "Task 3").  Per 128-dim block of the latent: scale = amax / 448 in fp32
+ * The row format above, written from fp32 values (the FP8 latent cache and a
+ * fused epilogue that would produce it are named in "Inside the Decode
+ * Performance Investigation", sections "Task 1" and "Task 3").  Per 128-dim block of the latent: scale = amax / 448 in fp32
  * (1.0 for an all-zero block) and code = e4m3(x / scale), rounded to nearest
  * with ties to even and saturated at +-448.  Rope values, and the bf16
  * format's latent, are rounded to bf16 (nearest, ties to even).  Token n is
@@ -256,14 +255,19 @@ int oracle_decode(int B, int H, int topk, int max_pages, int64_t pool_pages, int
  */
 
 /* fp32 -> OCP e4m3fn code: nearest value, ties to the even code, |x| beyond
- * the largest finite value (448) saturating to it.  Normal codes hold
- * (1 + m/8) * 2^(E-7) for E = 1..15 (E = 15 only up to m = 6); subnormal codes
- * hold m * 2^-9. */
+ * the largest finite value (448) saturating to it, infinities included (the
+ * format has none); NaN gives the format's NaN code S.1111.111.  Normal codes
+ * hold (1 + m/8) * 2^(E-7) for E = 1..15 (E = 15 only up to m = 6); subnormal
+ * codes hold m * 2^-9. */
 uint8_t oracle_e4m3_encode(float v) {
     const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7f);
     const double a = fabs((double)v);
     if (a == 0.0)
         return sign;
+    if (isinf(a))
+        return (uint8_t)(sign | 0x7e);            /* 448 */
     if (a < 0x1p-6) {
         /* subnormal range: a multiple of 2^-9; 8 * 2^-9 is the smallest normal (code 0x08) */
         return (uint8_t)(sign | (uint8_t)nearbyint(a * 512.0));
@@ -355,9 +359,9 @@ int oracle_kv_append(int n, int B, int max_pages, int64_t pool_pages, int kv_for
  * The step that produces topk_idx.  The pages name the indexer (its launches per
  * step: "Inside the Decode Performance Investigation", sections "The Setup" and
  * "Task 2") but give no formula; this follows the published lightning indexer
- * of DeepSeek's sparse attention, restated (a reading listed in the design
- * notes): for request b with indexer queries q[j][0..DI) and head weights w[j]
- * (j < HI), every context position s < ctx_len[b] whose page is valid scores
+ * of DeepSeek's sparse attention, restated (a reading, since the pages are
+ * silent): for request b with indexer queries q[j][0..DI) and head weights
+ * w[j] (j < HI), every context position s < ctx_len[b] whose page is valid scores
  *     I[s] = sum_j w[j] * max(0, sum_d q[j][d] * k_s[d])
  * with k_s the bf16 key row of s in its own paged cache (same page table as
  * the latent cache); the selection is the topk valid positions of largest I,

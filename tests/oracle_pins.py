@@ -358,7 +358,8 @@ def pin_query_tokens_share_selection(lib):
 
 def pin_e4m3_encode_roundtrip_ties_saturation(lib):
     """The encoder inverts the decoder on every finite code, sends each midpoint
-    between neighbouring codes to the even one, and saturates beyond 448."""
+    between neighbouring codes to the even one, saturates beyond 448 (infinities
+    too) and sends NaN to the NaN code."""
     vals = {}
     for c in range(256):
         if c & 0x7F == 0x7F:
@@ -375,8 +376,11 @@ def pin_e4m3_encode_roundtrip_ties_saturation(lib):
             assert oracle.e4m3_encode(np.float32(sgn * mid), lib) == (even | sb) if c0 != 0 or sgn == 1 else True
             assert oracle.e4m3_encode(np.nextafter(np.float32(sgn * mid), np.float32(sgn * 1e9)), lib) == (c1 | sb)
             assert oracle.e4m3_encode(np.nextafter(np.float32(sgn * mid), np.float32(0)), lib) == (c0 | sb)
-    for v in (448.0, 463.99, 464.0, 480.0, 1e5, 3.0e38):
+    for v in (448.0, 463.99, 464.0, 480.0, 1e5, 3.0e38, np.inf):
         assert oracle.e4m3_encode(np.float32(v), lib) == 0x7E and oracle.e4m3_encode(np.float32(-v), lib) == 0xFE
+    # the format has no infinities; its NaN is S.1111.111
+    assert oracle.e4m3_encode(np.float32(np.nan), lib) == 0x7F
+    assert oracle.e4m3_encode(-np.float32(np.nan), lib) == 0xFF
 
 
 def pin_encoders_match_torch_casts(lib):
