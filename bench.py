@@ -10,12 +10,22 @@ Headline workload: B = 80 requests x 64 heads, top-k 512 over a 131072-token
 context per request, fp8 e4m3 latent rows with per-128-dim block scales and
 bf16 rope, 70/30 recent/older index mix.  `--sets` independent seeded input
 sets (own Q, indices, page table and rows, each in its own region of one
-device pool) are cycled so successive calls gather cold rows: 16 sets touch
-~640 MB, more than the 256 MB Infinity Cache.
+device pool) are cycled without restarting between repeats, so a set comes
+back only after every other set has been read: 16 sets put ~610 MB between two
+reads of the same row, more than the 256 MB Infinity Cache.  Every pass below
+records that reuse distance; a figure is called cold only when it exceeds
+320 MiB.
 
-A second, shorter pass times the 512K-context uniform-index workload at
-B in {1, 8, 16, 32, 48, 64, 80, 88, 96} (cycling `--sweep-layers` layers) and
-reports per-layer us, the 42-layer step total and the per-request slope.
+Warm-up covers every input at least once and lasts at least 0.2 s of wall
+time, whatever --warmup says; the repeats' spread and any monotone trend are
+reported beside the median.
+
+A second pass times the 512K-context uniform-index workload at B in
+{1, 8, 16, 32, 48, 64, 80, 88, 96}: 16 layers with their own draws, each cut
+into disjoint batches of B requests, so every B cycles more than 320 MiB of
+rows; it reports per-layer us, the 42-layer step replayed from HIP graphs and
+the per-request slope.  --selector-sweep times the whole plan family at the
+same nine batch sizes and compares the selector's pick with the fastest.
 
 Prints ONE JSON line.  Timing uses HIP events on the launch stream.
 """
@@ -24,6 +34,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -38,13 +49,20 @@ METRIC = "sparse-MLA decode µs/layer + achieved HBM GB/s (% roofline) at B=1..9
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, vendor figure
+MALL_BYTES = 256 << 20         # Infinity Cache
+COLD_BYTES = 320 << 20         # reuse distance above which a pass counts as cold
+MIN_WARM_S = 0.2               # least wall time of every warm-up
 KERNEL_NAME = "split_kernel<1>"  # fp8 instantiation: the only kernel of a call
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_fp8_b80_ctx128k_traffic.json")
 SWEEP_B = (1, 8, 16, 32, 48, 64, 80, 88, 96)
+SWEEP_LAYERS = 16
 MTP_Q_LEN = (2, 4)
 APPEND_N = (80, 4096, 65536)
 MTP_B = (32, 80)
 LAYERS_PER_STEP = 42
+DTYPE = {0: "bf16 QK and PV MFMA (bf16 rows), fp32 accumulate",
+         1: "fp8-e4m3 latent QK MFMA with Q split into fp8 hi+lo (2 passes) + bf16 rope-QK and PV MFMA, "
+            "fp32 accumulate"}
 
 
 def kernel_source_hash() -> str:
@@ -55,27 +73,60 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic(w):
-    """(bytes, flops) one call must move / compute for workload w.
+def per_request_cost(w):
+    """Per request of workload w: (bytes, latent-QK flops, rope-QK flops, PV flops).
 
     Bytes read: every valid selected row (656 B fp8 / 1152 B bf16), the
     distinct page-table entries it needs, the top-k list, ctx_len and Q
-    (64 x 576 bf16 per request and query token).  Bytes written: out
-    (64 x 512 bf16) and lse (64 fp32) per request and query token.  Split-K
-    partials are not counted: they are this implementation's overhead, not
-    the method's.  With several query tokens the rows are counted once.
-    Flops: per valid (request, query token, head, row) 2*576 for QK^T and
-    2*512 for PV.
+    (64 x 576 bf16 per query token).  Bytes written: out (64 x 512 bf16) and
+    lse (64 fp32) per query token.  Split-K partials are not counted: they are
+    this implementation's overhead, not the method's.  With several query
+    tokens the rows are counted once.  Flops: per valid (query token, head,
+    row) 2*512 latent + 2*64 rope for QK^T and 2*512 for PV.
     """
     i = w.topk_idx.astype(np.int64)
     valid = (i >= 0) & (i < w.ctx_len[:, None])
-    n_valid = int(valid.sum())
-    pages = sum(len(np.unique(i[b][valid[b]] // 64)) for b in range(w.B))
-    B, T = w.B, w.q_len
-    rd = n_valid * w.row_bytes + 4 * pages + 4 * 512 * B + 4 * B + B * T * 64 * 576 * 2
-    wr = B * T * (64 * 512 * 2 + 64 * 4)
-    flops = n_valid * T * 64 * (2 * 576 + 2 * 512)
-    return int(rd + wr), int(flops)
+    nv = valid.sum(axis=1).astype(np.int64)
+    pages = np.array([len(np.unique(i[b][valid[b]] // 64)) for b in range(w.B)], dtype=np.int64)
+    T = w.q_len
+    byts = nv * w.row_bytes + 4 * pages + 4 * 512 + 4 + T * 64 * 576 * 2 + T * (64 * 512 * 2 + 64 * 4)
+    f = nv * T * 64
+    return byts, f * 2 * 512, f * 2 * 64, f * 2 * 512
+
+
+def cost_of(costs, lo=0, hi=None):
+    """Summed (bytes, latent, rope, pv) of requests lo..hi-1 from per_request_cost."""
+    return tuple(float(c[lo:hi].sum()) for c in costs)
+
+
+def mfma_report(cost, us, kv_format):
+    """Fraction of the measured time each MFMA class would need at its dense peak."""
+    _, f_lat, f_rope, f_pv = cost
+    t = us * 1e-6
+    if kv_format == 1:
+        lat = {"mfma": "fp8 e4m3 16x16x128, Q as hi+lo (2 passes)", "flops": int(f_lat), "executed_flops": int(2 * f_lat),
+               "frac_of_peak": round(2 * f_lat / t / (FP8_PEAK_TFLOPS * 1e12), 4), "peak_TFLOPs": FP8_PEAK_TFLOPS}
+    else:
+        lat = {"mfma": "bf16 16x16x32", "flops": int(f_lat), "executed_flops": int(f_lat),
+               "frac_of_peak": round(f_lat / t / (BF16_PEAK_TFLOPS * 1e12), 4), "peak_TFLOPs": BF16_PEAK_TFLOPS}
+    rope = {"mfma": "bf16 16x16x32", "flops": int(f_rope),
+            "frac_of_peak": round(f_rope / t / (BF16_PEAK_TFLOPS * 1e12), 4), "peak_TFLOPs": BF16_PEAK_TFLOPS}
+    pv = {"mfma": "bf16 32x32x16", "flops": int(f_pv),
+          "frac_of_peak": round(f_pv / t / (BF16_PEAK_TFLOPS * 1e12), 4), "peak_TFLOPs": BF16_PEAK_TFLOPS}
+    return {"qk_latent": lat, "qk_rope": rope, "pv": pv,
+            "busy_frac_at_peak": round(lat["frac_of_peak"] + rope["frac_of_peak"] + pv["frac_of_peak"], 4)}
+
+
+def repeat_stats(runs):
+    med = statistics.median(runs)
+    trend = "none"
+    if len(runs) >= 3:
+        if all(a > b for a, b in zip(runs, runs[1:])):
+            trend = "falling"
+        elif all(a < b for a, b in zip(runs, runs[1:])):
+            trend = "rising"
+    return {"repeats_us": [round(r, 3) for r in runs], "median_us": round(med, 3),
+            "spread": round((max(runs) - min(runs)) / med, 4), "trend": trend}
 
 
 def main() -> int:
@@ -87,7 +138,6 @@ def main() -> int:
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--nsplit", type=int, default=0, help="force the split count (0 = selector)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the B = 1..96 pass")
-    ap.add_argument("--sweep-layers", type=int, default=4)
     ap.add_argument("--sweep-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mtp", action="store_true", help="skip the several-query-tokens pass")
@@ -97,10 +147,11 @@ def main() -> int:
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other standard workloads (B=1 bf16, B=32, B=96 ragged)")
     ap.add_argument("--selector-sweep", action="store_true",
-                    help="time every split count and merge placement at B = 1..80 on the headline input sets "
-                         "and compare the selector's pick with the measured best")
+                    help="time every plan of the family at B = 1..96 on the sweep inputs and compare the "
+                         "selector's pick with the measured best")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+                    help="accepted for profiling commands: the plain 1 GiB device copy (which scales HBM byte "
+                         "counters) always runs first")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -111,31 +162,59 @@ def main() -> int:
     import torch
     import sparse_mla_top_amd as smla
     import workloads as W
-    from workloads.device import upload
+    from workloads.device import request_slice, upload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
 
+    def timed(step, n):
+        """us per call of n calls of step() on the launch stream (HIP events)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / n
+
+    def warm(step, n_min, min_s=MIN_WARM_S):
+        """Calls step() at least n_min times and for at least min_s seconds; returns the count."""
+        t0, n = time.time(), 0
+        while n < n_min or time.time() - t0 < min_s:
+            for _ in range(32):
+                step()
+            n += 32
+            torch.cuda.synchronize()
+        return n
+
+    def rotation(inputs, fn):
+        """step() that applies fn to the inputs in turn, never restarting."""
+        k = [0]
+
+        def step():
+            fn(inputs[k[0] % len(inputs)])
+            k[0] += 1
+        return step
+
+    def decode(d, shp, pl, w_s, o, l_, st=None):
+        rc = smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l_, shp, pl, w_s,
+                             stream=st or stream)
+        if rc != 0:
+            raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
+
     # A plain 1 GiB device-to-device copy: its read + write rate is the HBM
     # bandwidth a streaming kernel reaches on this device, reported beside the
-    # vendor peak.  (With --copy-calibration, run under rocprofv3's byte
-    # counters, the same copies scale FETCH_SIZE and WRITE_SIZE.)
+    # vendor peak (and, under rocprofv3's byte counters, the scale of
+    # FETCH_SIZE and WRITE_SIZE).
     x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     for _ in range(3):
         y.copy_(x)
-    torch.cuda.synchronize()
-    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    copy_ms = []
-    for _ in range(5):
-        ce0.record(stream)
-        y.copy_(x)
-        ce1.record(stream)
-        ce1.synchronize()
-        copy_ms.append(ce0.elapsed_time(ce1))
-    copy_gbs = 2 * x.numel() / (statistics.median(copy_ms) * 1e-3) / 1e9
+    copy_us = statistics.median(timed(lambda: y.copy_(x), 1) for _ in range(5))
+    copy_gbs = 2 * x.numel() / (copy_us * 1e-6) / 1e9
     log(f"device copy: {copy_gbs:.0f} GB/s read + write")
     del x, y
 
@@ -157,46 +236,33 @@ def main() -> int:
 
     w0 = sets[0][0]
     B = w0.B
+    costs = [per_request_cost(w) for w, _ in sets]
+    set_cost = [cost_of(c) for c in costs]
+    reuse_bytes = sum(c[0] for c in set_cost)
     shape = smla.make_shape(B, w0.kv_format, w0.max_pages, pool_pages)
     plan, ws_bytes = smla.plan_for(shape, args.nsplit or None)
     ws = smla.new_workspace(ws_bytes, dev)
     out = torch.empty((B, 64, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, 64), dtype=torch.float32, device=dev)
-
-    def call(d, shp, pl, w_s, o, l_):
-        rc = smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l_, shp, pl, w_s,
-                             stream=stream)
-        if rc != 0:
-            raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
-
-    def timed(fn, steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for k in range(steps):
-            fn(k)
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) * 1000.0 / steps     # us per call
-
-    for k in range(args.warmup):
-        call(sets[k % L][1], shape, plan, ws, out, lse)
-    torch.cuda.synchronize()
-    runs = [timed(lambda k: call(sets[k % L][1], shape, plan, ws, out, lse), args.steps)
-            for _ in range(args.repeats)]
-    full_us = statistics.median(runs)
-    log(f"B={B} plan={plan.as_dict()} us/call per repeat: {[round(r, 2) for r in runs]}")
+    step = rotation([d for _, d in sets], lambda d: decode(d, shape, plan, ws, out, lse))
+    tw = time.time()
+    warm_calls = warm(step, max(args.warmup, L))
+    warm_s = time.time() - tw
+    runs = [timed(step, args.steps) for _ in range(args.repeats)]
+    head = repeat_stats(runs)
+    full_us = head["median_us"]
+    log(f"B={B} plan={plan.as_dict()} warm-up {warm_calls} calls / {warm_s:.2f}s; us/call per repeat: "
+        f"{head['repeats_us']} spread {head['spread']:.3f} trend {head['trend']}")
     # input set 0's result, compared with the oracle in the CPU-baseline leg
-    call(sets[0][1], shape, plan, ws, out, lse)
+    decode(sets[0][1], shape, plan, ws, out, lse)
     torch.cuda.synchronize()
     out0 = out.float().cpu().numpy().astype(np.float64)
     lse0 = lse.cpu().numpy().astype(np.float64)
 
-    alg = [algorithmic(w) for w, _ in sets]
-    call_bytes = float(np.mean([a[0] for a in alg]))
-    call_flops = float(np.mean([a[1] for a in alg]))
+    call_cost = tuple(float(np.mean([c[j] for c in set_cost])) for j in range(4))
+    call_bytes = call_cost[0]
     achieved = call_bytes / (full_us * 1e-6) / 1e9
-    roof_us = max(call_bytes / (HBM_PEAK_GBS * 1e9), call_flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6
+    roof_us = call_bytes / (HBM_PEAK_GBS * 1e9) * 1e6
 
     traffic, traffic_note = None, "no counter file for this kernel source"
     if os.path.exists(TRAFFIC_FILE):
@@ -209,97 +275,17 @@ def main() -> int:
             traffic = t.get("hbm_bytes_per_launch")
             traffic_note = t.get("note", "")
 
-    # ------------------------------------------------------------------ selector check
-    # Every split count with no empty split and both merge placements, timed at
-    # B = 1 .. 80 on the first B requests of the same cold input sets; the
-    # selector's pick is compared with the measured best.
-    selector = None
-    if args.selector_sweep:
-        t4 = time.time()
-        selector = {}
-        for Bs in [b for b in SWEEP_B if b <= B]:
-            shp = smla.make_shape(Bs, w0.kv_format, w0.max_pages, pool_pages)
-            o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
-            l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
-            subs = [(d.q[:Bs], d.page_table[:Bs], d.topk_idx[:Bs], d.ctx_len[:Bs], d.scale) for _, d in sets]
-
-            def time_plan(pl):
-                p_, wsb = smla.plan_for(shp, pl)
-                w_s = smla.new_workspace(wsb, dev)
-
-                def scall(k):
-                    q_, pt_, ti_, cl_, sc_ = subs[k % L]
-                    rc = smla.decode_raw(q_, pool, pt_, ti_, cl_, sc_, o, l_, shp, pl, w_s, stream=stream)
-                    if rc != 0:
-                        raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
-                for k in range(10):
-                    scall(k)
-                return p_, statistics.median(timed(scall, args.sweep_steps) for _ in range(3))
-            def label(p_):   # split count / merge placement of a plan as returned
-                where = {smla.MERGE_IN_KERNEL: "in-kernel", smla.MERGE_SEPARATE: "separate"}.get(p_.merge, "-")
-                return f"{p_.nsplit}/{where}"
-            pick, pick_us = time_plan(None)
-            table = {}
-            for ns in (1, 2, 3, 4, 6, 8, 16):
-                for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
-                    p_, us = time_plan({"nsplit": ns, "merge": merge})
-                    table[label(p_)] = round(us, 2)
-            best = min(table, key=table.get)
-            selector[str(Bs)] = {"pick": label(pick), "pick_us": round(pick_us, 2), "best": best,
-                                 "best_us": table[best], "pick_over_best": round(pick_us / table[best], 3),
-                                 "all_us": table}
-        log(f"selector sweep done in {time.time() - t4:.1f}s: "
-            f"{ {b: (v['pick'], v['best'], v['pick_over_best']) for b, v in selector.items()} }")
-
-    # ------------------------------------------------------------------ the other standard workloads
-    # B=1 with bf16 rows (4096-token context), B=32 (65536), B=96 ragged
-    # (log-uniform contexts from 128 to 524288, -1 padding): 8 cold input sets
-    # each in one pool, automatic plan, as for the headline.
-    configs = None
-    if not args.no_configs:
-        t5 = time.time()
-        configs = {}
-        Lc = 8
-        for wid in (1, 2, 4):
-            wl, base = [], 0
-            for l in range(Lc):
-                w = W.make(wid, layer=l, page_base=base)
-                wl.append(w)
-                base = w.pool_pages
-            cpool = torch.zeros(base * W.PAGE * wl[0].row_bytes, dtype=torch.uint8, device=dev)
-            dl = [upload(w, dev, pool=cpool) for w in wl]
-            shapes = [smla.make_shape(w.B, w.kv_format, w.page_table.shape[1], base) for w in wl]
-            cplan, cwsb = smla.plan_for(shapes[0])
-            cws = smla.new_workspace(cwsb, dev)
-            co = torch.empty((wl[0].B, 64, 512), dtype=torch.bfloat16, device=dev)
-            cl = torch.empty((wl[0].B, 64), dtype=torch.float32, device=dev)
-
-            def ccall(k):
-                call(dl[k % Lc], shapes[k % Lc], cplan, cws, co, cl)
-            for k in range(10):
-                ccall(k)
-            us = statistics.median(timed(ccall, args.sweep_steps) for _ in range(3))
-            cb = float(np.mean([algorithmic(w)[0] for w in wl]))
-            cf = float(np.mean([algorithmic(w)[1] for w in wl]))
-            configs[wl[0].name] = {
-                "B": wl[0].B, "kv_format": "bf16" if wl[0].kv_format == W.FMT_BF16 else "fp8", "us_per_layer": round(us, 2),
-                "plan": cplan.as_dict(), "algorithmic_bytes": int(cb), "GBps": round(cb / (us * 1e-6) / 1e9, 1),
-                "hbm_frac": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "mfma_frac_bf16_peak": round(cf / (us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4)}
-            del dl, cpool, cws
-            torch.cuda.empty_cache()
-        log(f"other workloads done in {time.time() - t5:.1f}s: "
-            f"{ {k: (v['us_per_layer'], v['hbm_frac']) for k, v in configs.items()} }")
-
     # ------------------------------------------------------------------ query tokens
-    # q_len query tokens per request sharing its selection, on the same cold
-    # input sets (extra Q per token; the rows are those of the headline sets)
+    # q_len query tokens per request sharing its selection, on the headline
+    # sets cut into disjoint batches of B requests (extra Q per token; the rows
+    # are those of the headline sets)
     mtp = None
     if not args.no_mtp:
         t2 = time.time()
         mtp = {}
         for T in MTP_Q_LEN:
             qs = [torch.from_numpy(W.with_query_tokens(w, T).q).to(dev).view(torch.bfloat16) for w, _ in sets]
+            qcosts = [per_request_cost(W.with_query_tokens(w, T)) for w, _ in sets]
             per = {}
             for Bm in MTP_B:
                 shp = smla.make_shape(Bm, w0.kv_format, w0.max_pages, pool_pages, T)
@@ -307,56 +293,121 @@ def main() -> int:
                 w_s = smla.new_workspace(wsb, dev)
                 o = torch.empty((Bm, T, 64, 512), dtype=torch.bfloat16, device=dev)
                 l_ = torch.empty((Bm, T, 64), dtype=torch.float32, device=dev)
+                ins, cs = [], []
+                for si, (_, d) in enumerate(sets):
+                    for g in range(B // Bm):
+                        ds = request_slice(d, g * Bm, (g + 1) * Bm)
+                        ins.append((ds, qs[si][g * Bm:(g + 1) * Bm]))
+                        cs.append(cost_of(qcosts[si], g * Bm, (g + 1) * Bm))
 
-                def mcall(k):
-                    d = sets[k % L][1]
-                    rc = smla.decode_raw(qs[k % L][:Bm], d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale,
-                                         o, l_, shp, pl, w_s, stream=stream)
+                def mcall(x):
+                    ds, q_ = x
+                    rc = smla.decode_raw(q_, ds.pool, ds.page_table, ds.topk_idx, ds.ctx_len, ds.scale, o, l_, shp,
+                                         pl, w_s, stream=stream)
                     if rc != 0:
                         raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
-                for k in range(10):
-                    mcall(k)
-                us = statistics.median(timed(mcall, args.sweep_steps) for _ in range(3))
-                byts = float(np.mean([algorithmic(W.with_query_tokens(w.subset(Bm), T))[0] for w, _ in sets[:4]]))
-                per[str(Bm)] = {"us_per_layer": round(us, 2), "us_per_query_token": round(us / T, 2),
+                mstep = rotation(ins, mcall)
+                warm(mstep, len(ins), 0.05)
+                st = repeat_stats([timed(mstep, args.sweep_steps) for _ in range(3)])
+                us = st["median_us"]
+                byts = float(np.mean([c[0] for c in cs]))
+                per[str(Bm)] = {"us_per_layer": us, "us_per_query_token": round(us / T, 2),
                                 "nsplit": pl.nsplit, "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                                "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                                "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "inputs": len(ins), "reuse_distance_MB": round(sum(c[0] for c in cs) / 1e6, 1),
+                                "spread": st["spread"]}
             mtp[str(T)] = per
             del qs
         log(f"query-token pass done in {time.time() - t2:.1f}s: {mtp}")
 
+    # ------------------------------------------------------------------ the other standard workloads
+    # B=1 with bf16 rows (4096-token context), B=32 (65536), B=96 ragged
+    # (log-uniform contexts from 128 to 524288, -1 padding): as many independent
+    # draws as put more than 320 MiB between two reads of a row, in one pool
+    # with only the pages that hold a selected token (the work per call is the
+    # same as with every page present), automatic plan.
+    configs = None
+    if not args.no_configs:
+        t5 = time.time()
+        configs = {}
+        for wid in (1, 2, 4):
+            first = W.make(wid, compact=True)
+            per_call = cost_of(per_request_cost(first))[0]
+            n_draws = max(4, min(512, math.ceil(COLD_BYTES / per_call)))
+            wl, base = [], 0
+            for l in range(n_draws):
+                w = W.make(wid, layer=l, compact=True, page_base=base)
+                wl.append(w)
+                base = w.pool_pages
+            cpool = torch.zeros(base * W.PAGE * wl[0].row_bytes, dtype=torch.uint8, device=dev)
+            dl = [upload(w, dev, pool=cpool) for w in wl]
+            cc = [cost_of(per_request_cost(w)) for w in wl]
+            shapes = [smla.make_shape(w.B, w.kv_format, w.page_table.shape[1], base) for w in wl]
+            cplan, cwsb = smla.plan_for(shapes[0])
+            cws = smla.new_workspace(cwsb, dev)
+            co = torch.empty((wl[0].B, 64, 512), dtype=torch.bfloat16, device=dev)
+            cl = torch.empty((wl[0].B, 64), dtype=torch.float32, device=dev)
+            cstep = rotation(list(zip(dl, shapes)), lambda x: decode(x[0], x[1], cplan, cws, co, cl))
+            warm(cstep, n_draws, 0.05)
+            st = repeat_stats([timed(cstep, max(args.sweep_steps, n_draws)) for _ in range(3)])
+            us = st["median_us"]
+            mean_cost = tuple(float(np.mean([c[j] for c in cc])) for j in range(4))
+            cb = mean_cost[0]
+            configs[wl[0].name] = {
+                "B": wl[0].B, "kv_format": "bf16" if wl[0].kv_format == W.FMT_BF16 else "fp8", "us_per_layer": us,
+                "spread": st["spread"], "plan": cplan.as_dict(), "algorithmic_bytes": int(cb),
+                "GBps": round(cb / (us * 1e-6) / 1e9, 1), "hbm_frac": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "draws": n_draws, "reuse_distance_MB": round(sum(c[0] for c in cc) / 1e6, 1),
+                "mfma": mfma_report(mean_cost, us, wl[0].kv_format)}
+            del dl, cpool, cws
+            torch.cuda.empty_cache()
+        log(f"other workloads done in {time.time() - t5:.1f}s: "
+            f"{ {k: (v['us_per_layer'], v['hbm_frac'], v['reuse_distance_MB']) for k, v in configs.items()} }")
+
     # ------------------------------------------------------------------ cache producer
-    # smla_kv_append writing n new tokens' fp8 rows for 80 requests (token i: request
-    # i % 80, next position) into a separate pool whose pages are a random permutation
+    # smla_kv_append writing n new tokens' fp8 rows for 80 requests (token i:
+    # request i % 80, next position) into a pool whose pages are a random
+    # permutation.  The calls walk through windows of one token stream long
+    # enough that its inputs total more than 320 MiB, each window writing its
+    # own positions, so no call re-reads a window still in the Infinity Cache.
     append = None
     if not args.no_append:
         append = {}
         g = torch.Generator(device=dev).manual_seed(7)
+        in_bytes = 512 * 4 + 64 * 4 + 4 + 4
         for n in APPEND_N:
             Ba = 80
-            per_req = (n + Ba - 1) // Ba
+            windows = max(2, math.ceil(COLD_BYTES / (n * in_bytes)))
+            total = windows * n
+            per_req = (total + Ba - 1) // Ba
             npg = (per_req + W.PAGE - 1) // W.PAGE
             apool_pages = Ba * npg
             apool = torch.zeros(apool_pages * W.PAGE * 656, dtype=torch.uint8, device=dev)
             apt = torch.randperm(apool_pages, generator=g, device=dev).to(torch.int32).view(Ba, npg)
-            lat = torch.randn((n, 512), generator=g, device=dev, dtype=torch.float32)
-            rope = torch.randn((n, 64), generator=g, device=dev, dtype=torch.float32)
-            ar = torch.arange(n, device=dev, dtype=torch.int32)
+            lat = torch.randn((total, 512), generator=g, device=dev, dtype=torch.float32)
+            rope = torch.randn((total, 64), generator=g, device=dev, dtype=torch.float32)
+            ar = torch.arange(total, device=dev, dtype=torch.int32)
             req, pos = (ar % Ba).contiguous(), (ar // Ba).contiguous()
             ashape = smla.make_shape(Ba, W.FMT_FP8, npg, apool_pages)
+            wins = [(lat[j * n:(j + 1) * n], rope[j * n:(j + 1) * n], req[j * n:(j + 1) * n], pos[j * n:(j + 1) * n])
+                    for j in range(windows)]
 
-            def acall(k):
-                rc = smla.kv_append_raw(lat, rope, req, pos, apt, apool, ashape, stream)
+            def acall(x):
+                rc = smla.kv_append_raw(x[0], x[1], x[2], x[3], apt, apool, ashape, stream)
                 if rc != 0:
                     raise RuntimeError(f"kv_append failed: {smla.strerror(rc)}")
-            for k in range(10):
-                acall(k)
-            us = statistics.median(timed(acall, 200) for _ in range(3))
-            byts = n * (512 * 4 + 64 * 4 + 4 + 4 + 4 + 656)
-            append[str(n)] = {"us": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+            astep = rotation(wins, acall)
+            warm(astep, windows, 0.05)
+            st = repeat_stats([timed(astep, max(50, windows)) for _ in range(3)])
+            us = st["median_us"]
+            byts = n * (in_bytes + 4 + 656)
+            append[str(n)] = {"us": us, "spread": st["spread"], "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                               "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                              "algorithmic_bytes": byts}
-            del apool, lat, rope
+                              "frac_of_device_copy": round(byts / (us * 1e-6) / 1e9 / copy_gbs, 4),
+                              "algorithmic_bytes": byts, "windows": windows,
+                              "reuse_distance_MB": round(windows * n * in_bytes / 1e6, 1)}
+            del apool, lat, rope, wins
+            torch.cuda.empty_cache()
         log(f"cache-producer pass: {append}")
 
     # ------------------------------------------------------------------ top-k indexer
@@ -378,18 +429,18 @@ def main() -> int:
         iidx = torch.empty((Bi, 512), dtype=torch.int32, device=dev)
         ishape = smla.make_shape(Bi, W.FMT_FP8, mp, ipool_pages)
 
-        def icall(k):
+        def icall():
             rc = smla.indexer_topk_raw(qi, wi, keys, ipt, ctxi, isc, iidx, ishape, stream)
             if rc != 0:
                 raise RuntimeError(f"indexer failed: {smla.strerror(rc)}")
-        for k in range(3):
-            icall(k)
-        us = statistics.median(timed(icall, 20) for _ in range(3))
+        warm(icall, 3, 0.05)
+        st = repeat_stats([timed(icall, 20) for _ in range(3)])
+        us = st["median_us"]
         pages = Bi * mp
         byts = Bi * ctx_i * (128 * 2 + 4) + 4 * pages + Bi * (64 * 128 * 2 + 64 * 4 + 4 + 512 * 4)
         flops = Bi * ctx_i * 64 * 128 * 2
         indexer = {"kernel": "indexer_score_kernel + indexer_select_kernel", "B": Bi, "ctx_len": ctx_i,
-                   "heads": 64, "head_dim": 128, "key_format": "bf16", "us": round(us, 2),
+                   "heads": 64, "head_dim": 128, "key_format": "bf16", "us": us, "spread": st["spread"],
                    "algorithmic_bytes": int(byts), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
                    "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "frac_of_device_copy": round(byts / (us * 1e-6) / 1e9 / copy_gbs, 4),
@@ -398,72 +449,128 @@ def main() -> int:
         torch.cuda.empty_cache()
         log(f"indexer pass done in {time.time() - t3:.1f}s: {indexer}")
 
-    # ------------------------------------------------------------------ B sweep
+    # ------------------------------------------------------------------ B sweep (+ selector check)
     sweep = None
-    if not args.no_sweep:
+    selector = None
+    if not args.no_sweep or args.selector_sweep:
         t1 = time.time()
         del sets
         pool = None
         torch.cuda.empty_cache()
-        Ls = args.sweep_layers
-        full = []
-        spool, per = None, None
-        for l in range(Ls):
-            w = W.make(5, layer=l, page_base=0 if per is None else l * per)
-            if per is None:
-                per = w.pool_pages
-                w = W.make(5, layer=0, page_base=0)
-                spool = torch.empty(per * Ls * W.PAGE * w.row_bytes, dtype=torch.uint8, device=dev)
+        full, dfull, base = [], [], 0
+        for l in range(SWEEP_LAYERS):
+            w = W.make(5, layer=l, page_base=base)
             full.append(w)
-        log(f"generated {Ls} layers of {full[0].name} in {time.time() - t1:.1f}s")
-        per_b = {}
-        for Bs in SWEEP_B:
-            subs = [upload(w.subset(Bs), dev, pool=spool) for w in full]
-            shp = smla.make_shape(Bs, full[0].kv_format, full[0].max_pages, per * Ls)
-            pl, wsb = smla.plan_for(shp)
-            w_s = smla.new_workspace(wsb, dev)
-            o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
-            l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
-            for k in range(10):
-                call(subs[k % Ls], shp, pl, w_s, o, l_)
-            us = statistics.median(timed(lambda k: call(subs[k % Ls], shp, pl, w_s, o, l_), args.sweep_steps)
-                                   for _ in range(3))
-            byts = float(np.mean([algorithmic(w.subset(Bs))[0] for w in full]))
-            # the 42-layer step captured as one HIP graph (layer l reads layer l % Ls's inputs)
-            gs = torch.cuda.Stream()
-            gs.wait_stream(stream)
-            graph = torch.cuda.CUDAGraph()
+            base = w.pool_pages
+        spool = torch.empty(base * W.PAGE * full[0].row_bytes, dtype=torch.uint8, device=dev)
+        dfull = [upload(w, dev, pool=spool) for w in full]
+        scosts = [per_request_cost(w) for w in full]
+        torch.cuda.synchronize()
+        log(f"generated {SWEEP_LAYERS} layers of {full[0].name} in {time.time() - t1:.1f}s "
+            f"(pool {spool.numel() / 2**30:.1f} GiB)")
 
-            def step_on(st):
-                for k in range(LAYERS_PER_STEP):
-                    d = subs[k % Ls]
-                    if smla.decode_raw(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l_, shp, pl,
-                                       w_s, stream=st) != 0:
-                        raise RuntimeError("decode failed during capture")
-            with torch.cuda.stream(gs):
-                step_on(gs)
+        def batches(Bs):
+            """Disjoint batches of Bs requests cut from every layer, and their costs."""
+            ins, cs = [], []
+            for li, d in enumerate(dfull):
+                for gi in range(full[0].B // Bs):
+                    ins.append(request_slice(d, gi * Bs, (gi + 1) * Bs))
+                    cs.append(cost_of(scosts[li], gi * Bs, (gi + 1) * Bs))
+            return ins, cs
+
+        if not args.no_sweep:
+            per_b = {}
+            for Bs in SWEEP_B:
+                ins, cs = batches(Bs)
+                shp = smla.make_shape(Bs, full[0].kv_format, full[0].max_pages, base)
+                pl, wsb = smla.plan_for(shp)
+                w_s = smla.new_workspace(wsb, dev)
+                o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
+                l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
+                sstep = rotation(ins, lambda d: decode(d, shp, pl, w_s, o, l_))
+                warm(sstep, len(ins), 0.05)
+                st = repeat_stats([timed(sstep, max(args.sweep_steps, len(ins) // 4)) for _ in range(3)])
+                us = st["median_us"]
+                mean_cost = tuple(float(np.mean([c[j] for c in cs])) for j in range(4))
+                byts = mean_cost[0]
+                # the 42-layer step as HIP graphs: graph g replays inputs 42g .. 42g+41 of the rotation, and
+                # the graphs are replayed in turn, so a replay reads rows no recent replay has read
+                gs = torch.cuda.Stream()
+                gs.wait_stream(stream)
+                n_graphs = min(40, math.ceil(len(ins) / LAYERS_PER_STEP))
+                graphs = []
+                for gi in range(n_graphs):
+                    layer_ins = [ins[(gi * LAYERS_PER_STEP + k) % len(ins)] for k in range(LAYERS_PER_STEP)]
+                    graph = torch.cuda.CUDAGraph()
+                    with torch.cuda.stream(gs):
+                        for d in layer_ins:
+                            decode(d, shp, pl, w_s, o, l_, gs)
+                        torch.cuda.synchronize()
+                        with torch.cuda.graph(graph, stream=gs):
+                            for d in layer_ins:
+                                decode(d, shp, pl, w_s, o, l_, gs)
+                    graphs.append(graph)
                 torch.cuda.synchronize()
-                with torch.cuda.graph(graph, stream=gs):
-                    step_on(gs)
-            torch.cuda.synchronize()
-            for _ in range(3):
-                graph.replay()
-            step_us = statistics.median(timed(lambda k: graph.replay(), 20) for _ in range(3))
-            del graph
-            per_b[Bs] = {"us_per_layer": round(us, 2), "nsplit": pl.nsplit,
-                         "GBps": round(byts / (us * 1e-6) / 1e9, 1),
-                         "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "graph_step_us_42_layers": round(step_us, 1)}
-            del subs
-        bs = np.array(SWEEP_B, dtype=float)
-        ys = np.array([per_b[b]["us_per_layer"] for b in SWEEP_B])
-        slope = float(np.polyfit(bs, ys, 1)[0])
-        sweep = {"workload": full[0].name, "ctx_len": int(full[0].ctx_len[0]), "layers_cycled": Ls,
-                 "per_B": {str(k): v for k, v in per_b.items()},
-                 "step_total_us_42_layers": {str(b): round(per_b[b]["us_per_layer"] * LAYERS_PER_STEP, 1)
-                                             for b in SWEEP_B},
-                 "slope_us_per_request_per_layer": round(slope, 3)}
-        log(f"sweep done in {time.time() - t1:.1f}s")
+                gstep = rotation(graphs, lambda gr: gr.replay())
+                warm(gstep, n_graphs, 0.05)
+                gst = repeat_stats([timed(gstep, max(10, n_graphs)) for _ in range(3)])
+                del graphs
+                per_b[Bs] = {"us_per_layer": us, "spread": st["spread"], "nsplit": pl.nsplit,
+                             "merge": pl.merge, "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             "inputs": len(ins), "reuse_distance_MB": round(sum(c[0] for c in cs) / 1e6, 1),
+                             "graph_step_us_42_layers": round(gst["median_us"], 1),
+                             "graph_us_per_layer": round(gst["median_us"] / LAYERS_PER_STEP, 2),
+                             "graphs": n_graphs, "mfma": mfma_report(mean_cost, us, full[0].kv_format)}
+                del ins, w_s
+            bs = np.array(SWEEP_B, dtype=float)
+            ys = np.array([per_b[b]["us_per_layer"] for b in SWEEP_B])
+            slope = float(np.polyfit(bs, ys, 1)[0])
+            sweep = {"workload": full[0].name, "ctx_len": int(full[0].ctx_len[0]), "layers": SWEEP_LAYERS,
+                     "per_B": {str(k): v for k, v in per_b.items()},
+                     "step_total_us_42_layers": {str(b): round(per_b[b]["us_per_layer"] * LAYERS_PER_STEP, 1)
+                                                 for b in SWEEP_B},
+                     "slope_us_per_request_per_layer": round(slope, 3)}
+            log(f"sweep done in {time.time() - t1:.1f}s: "
+                f"{ {b: (v['us_per_layer'], v['graph_us_per_layer'], v['reuse_distance_MB']) for b, v in per_b.items()} }")
+
+        # Every plan of the family (split count with no empty split x merge
+        # placement; heads per workgroup, tile tokens and workgroups per CU
+        # have one value each in this kernel) timed at every sweep batch size,
+        # and the selector's pick compared with the fastest.
+        if args.selector_sweep:
+            t4 = time.time()
+            selector = {}
+            for Bs in SWEEP_B:
+                ins, _ = batches(Bs)
+                shp = smla.make_shape(Bs, full[0].kv_format, full[0].max_pages, base)
+                o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
+                l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
+
+                def time_plan(pl):
+                    p_, wsb = smla.plan_for(shp, pl)
+                    w_s = smla.new_workspace(wsb, dev)
+                    pstep = rotation(ins, lambda d: decode(d, shp, pl, w_s, o, l_))
+                    warm(pstep, len(ins), 0.03)
+                    return p_, statistics.median(timed(pstep, max(args.sweep_steps, len(ins) // 4))
+                                                 for _ in range(3))
+
+                def label(p_):
+                    where = {smla.MERGE_IN_KERNEL: "in-kernel", smla.MERGE_SEPARATE: "separate"}.get(p_.merge, "-")
+                    return f"{p_.nsplit}/{where}/h{p_.heads_per_wg}/t{p_.tile_tokens}/wg{p_.wg_per_cu}"
+                pick, pick_us = time_plan(None)
+                table = {}
+                for ns in (1, 2, 3, 4, 6, 8, 16):
+                    for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
+                        p_, us = time_plan({"nsplit": ns, "merge": merge})
+                        table[label(p_)] = round(us, 2)
+                best = min(table, key=table.get)
+                selector[str(Bs)] = {"pick": label(pick), "pick_us": round(pick_us, 2), "best": best,
+                                     "best_us": table[best], "pick_over_best": round(pick_us / table[best], 3),
+                                     "all_us": table}
+            log(f"selector sweep done in {time.time() - t4:.1f}s: "
+                f"{ {b: (v['pick'], v['best'], v['pick_over_best']) for b, v in selector.items()} }")
+        del dfull, spool
 
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
@@ -503,16 +610,18 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 x bf16 mfma, fp32 accum",
+        "dtype": DTYPE[w0.kv_format],
         "data": "synthetic (seeded)",
         "config": {
             "workload": w0.name, "B": B, "heads": 64, "topk": 512, "ctx_len": int(w0.ctx_len[0]),
             "kv_format": "fp8_e4m3_block128+bf16_rope", "row_bytes": w0.row_bytes,
             "index_mix": "358 of the last 8192 tokens + 154 older, without replacement", "input_sets": L,
-            "plan": plan.as_dict(), "repeats_us": [round(r, 3) for r in runs],
-            "algorithmic_bytes_per_call": int(call_bytes), "algorithmic_flops_per_call": int(call_flops),
+            "reuse_distance_MB": round(reuse_bytes / 1e6, 1), "cold": reuse_bytes > COLD_BYTES,
+            "warmup_calls": warm_calls, "warmup_s": round(warm_s, 3),
+            "plan": plan.as_dict(), **head,
+            "algorithmic_bytes_per_call": int(call_bytes), "algorithmic_flops_per_call": int(sum(call_cost[1:])),
             "roofline_us_per_call": round(roof_us, 3),
-            "mfma_frac_bf16_peak": round(call_flops / (full_us * 1e-6) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "mfma": mfma_report(call_cost, full_us, w0.kv_format),
             "traffic_note": traffic_note,
             "sweep": sweep,
             "indexer_topk": indexer,
@@ -524,7 +633,8 @@ def main() -> int:
                 "per_n_tokens": append},
             "query_tokens": None if mtp is None else {
                 "workload": w0.name, "q_len": mtp,
-                "note": "q_len query tokens per request share its selection; same 16 cold input sets"},
+                "note": "q_len query tokens per request share its selection; the headline sets cut into "
+                        "disjoint batches"},
         },
         "roofline": {"kernel": KERNEL_NAME, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -26,8 +26,10 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
 
 // Source of masked rows: reading zeros keeps every MFMA operand finite.
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[kRowBytesBf16];
@@ -39,7 +41,7 @@ constexpr int kPRow = 24;        // bf16 per P^T row in LDS (16 tokens + 8 pad: 
 template <int FMT> struct RowFmt;
 template <> struct RowFmt<kFmtFp8> {
   static constexpr int kRow = kRowBytesFp8;   // 512 e4m3 | 16 B scales | 128 B rope
-  static constexpr int kNbuf = 6;             // 6 x 20,992 B of LDS tiles
+  static constexpr int kNbuf = 4;             // 4 x 20,992 B of LDS tiles
 };
 template <> struct RowFmt<kFmtBf16> {
   static constexpr int kRow = kRowBytesBf16;  // 576 bf16
@@ -396,6 +398,65 @@ __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, co
     }
 }
 
+// The row loads of one split on one loader wave: NT tiles, N 16-byte loads
+// per lane and tile (instructions v, v + 4, ... of each tile, as DmaCount
+// deals them to 4 waves), staged in registers and written to LDS buffer
+// t % NBUF just before the barrier that publishes tile t.  Tile t sits in
+// register slot t % S from its load to its write, which frees the slot for
+// tile t + S (S = 3 for fp8 rows, 2 for the larger bf16 rows).  Everything is
+// unrolled on the compile-time tile count, so the compiler's waits before
+// each write count exactly the loads issued after it (loads complete in issue
+// order) and the next S - 1 tiles stay in flight.
+// Lanes past the tile's last slot (the last fp8 instruction is half full)
+// repeat that slot: same source, same bytes, same LDS address.
+// Barrier k of the loop follows the write of tile k + 1 (PIPE: the QK waves
+// read a tile ahead; tile 0 also before barrier 0) or tile k; NT + 1 barriers
+// in all, as every other wave takes.
+template <int FMT, int N, int NT, bool PIPE>
+__device__ __forceinline__ void load_rows(const uint64_t LDS_AS* rowaddr_s, uint8_t LDS_AS* tiles, int v, int lane) {
+  using TL = TileLayout<FMT>;
+  constexpr int kNbufR = RowFmt<FMT>::kNbuf;
+  constexpr int kTileBytes = kTile * RowFmt<FMT>::kRow;
+  constexpr int S = FMT == kFmtFp8 ? 3 : 1;
+  u32x4 reg[S][N];
+  uint32_t dst[N];   // byte offset of this lane's 16 bytes of instruction q in a tile
+#pragma unroll
+  for (int q = 0; q < N; ++q) dst[q] = 16u * (uint32_t)min(64 * (v + 4 * q) + lane, TL::kSlots - 1);
+  auto load = [&](int t, u32x4 (&d)[N]) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const int slot = (int)(dst[q] >> 4);
+      const int row = slot / TL::kChunksRow, chunk = slot - row * TL::kChunksRow;
+      const uint64_t src = (rowaddr_s[t * kTile + row] & ~1ull) + 16 * chunk;
+      d[q] = *reinterpret_cast<const u32x4 GLOBAL_AS*>(static_cast<uintptr_t>(src));
+    }
+  };
+  auto write = [&](int t, const u32x4 (&d)[N]) {
+    uint8_t LDS_AS* base = tiles + (t % kNbufR) * kTileBytes;
+#pragma unroll
+    for (int q = 0; q < N; ++q) *reinterpret_cast<u32x4 LDS_AS*>(base + dst[q]) = d[q];
+  };
+#pragma unroll
+  for (int t = 0; t < (NT < S ? NT : S); ++t) load(t, reg[t]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    write(t, reg[t % S]);
+    if (t + S < NT) load(t + S, reg[t % S]);
+    if (!PIPE || t > 0) lds_barrier();
+  }
+  // the barriers left: k = NT - 1 and NT (PIPE), or k = NT
+  if (PIPE) lds_barrier();
+  lds_barrier();
+}
+
+// load_rows for loader wave v (0 .. 3) of a split of NT tiles.
+template <int FMT, bool PIPE, int NT>
+__device__ __forceinline__ void load_rows_nt(const uint64_t LDS_AS* rowaddr_s, uint8_t LDS_AS* tiles, int v, int lane) {
+  using Ld = DmaCount<FMT, kLdWaves>;
+  if (v < Ld::kRichWaves) load_rows<FMT, Ld::kPerWave, NT, PIPE>(rowaddr_s, tiles, v, lane);
+  else load_rows<FMT, Ld::kPoor, NT, PIPE>(rowaddr_s, tiles, v, lane);
+}
+
 // ----------------------------------------------------------------------------
 // Split kernel.  512 threads = 8 waves, one workgroup per (request, split),
 // with two roles that run side by side on each SIMD (waves w and w+4 share
@@ -432,6 +493,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // One LDS block: the tile ring, then P^T.  A merging workgroup reuses its
   // first 128 KB for its own partial output.
   constexpr int kRingBytes = kNbuf * kTileBytes;
+  constexpr int kQBytes = kHpw * kDqk * 2;
+  constexpr int kQOff = kRingBytes - kQBytes;      // Q staging: the end of the ring
   // P^T copies: one per 128-dim scale block (fp8 rows: P times that block's
   // scale) or a single one (bf16 rows)
   constexpr int kPCopies = FMT == kFmtFp8 ? 4 : 1;
@@ -474,6 +537,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   const int tile0 = s * a.chunk_tiles;
   if (tile0 >= kTiles) return;   // empty split (the host never launches one)
   const int ntiles = min(a.chunk_tiles, kTiles - tile0);
+  // the loader waves are specialised on these counts (the host only forms
+  // splits of 16 / nsplit tiles rounded up, nsplit in 1, 2, 3, 4, 6, 8, 16);
+  // any other count leaves the whole workgroup before its first barrier
+  if (ntiles != 16 && ntiles != 8 && ntiles != 6 && ntiles != 4 && ntiles != 3 && ntiles != 2 && ntiles != 1)
+    return;
   const int ntok = ntiles * kTile;
   const int ctx = a.ctx_len[b];
   const bool fused = a.nsplit > 1 && a.counters != nullptr;   // merge in this launch
@@ -508,71 +576,34 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   }
   static_assert(64 * (kPvWaves + kLdWaves) >= kTopk, "the translating waves cover every top-k slot");
 
-  // ---- 3. row loads.  The first npre tiles go out at once, issued by the PV
-  // and loader waves together; every later tile is issued by the loader waves
-  // alone, one per iteration.  A direct-to-LDS load holds its issuing wave
-  // for a long time when the memory path is busy, so no wave that computes
-  // issues a load inside the loop.
+  // ---- 3. row loads.  The loader waves alone move the rows: plain global
+  // loads into registers, kLdSlots tiles ahead, each tile written to its LDS
+  // buffer with ds_write just before the barrier that publishes it.  (A
+  // direct-to-LDS load, while the memory path is busy, stalls the LDS reads of
+  // the other waves of the compute unit; a register-staged tile costs the LDS
+  // one short burst of writes.)  In iteration k the QK waves start tile k+1
+  // and finish tile k, and the PV waves accumulate tile k-1 and read the V
+  // operands of tile k, so tile k+2 is written during iteration k into the
+  // buffer of tile k-2, whose last reads completed before barrier k.  Without
+  // the QK look-ahead (bf16 rows: a ring of 3 buffers) tile k+1 is written
+  // during iteration k into the buffer of tile k-2.
   const bool ld_role = wave >= kQkWaves + kPvWaves;
-  const int iw = qk_role ? 0 : wave - kQkWaves;             // first-burst issuer 0 .. 7
   const int lw = ld_role ? wave - kQkWaves - kPvWaves : 0;  // loader 0 .. 3
-  constexpr int kInitIssuers = kPvWaves + kLdWaves;
-  using InitDma = DmaCount<FMT, kInitIssuers>;
-  using LdDma = DmaCount<FMT, kLdWaves>;
-  // In iteration k the QK waves start tile k+1 and finish tile k, and the PV
-  // waves accumulate tile k-1; tile k + kAhead is issued in iteration k
-  // into the buffer of tile k - 2 (finished at k - 2, accumulated at k - 1,
-  // so free after the barrier of iteration k - 1).
-  constexpr int kAhead = kNbuf - 2;
-  // The QK look-ahead needs tile k+1 issued before iteration k, i.e. a ring of
-  // at least 4 buffers (fp8 rows: 6; bf16 rows fit only 3 and run unpipelined,
-  // tile k scored and finished in iteration k).
   constexpr bool kPipe = kNbuf >= 4;
-  const int npre = min(kAhead, ntiles);
-  auto tile_lds = [&](int tt) { return (uint8_t LDS_AS*)(tiles + (tt % kNbuf) * kTileBytes); };
-  if (!qk_role)
-    for (int tt = 0; tt < npre; ++tt)
-      issue_tile<FMT, kInitIssuers>(
-          tile_src<FMT, kInitIssuers>((const uint64_t LDS_AS*)rowaddr_s, tt * kTile, iw, lane), tile_lds(tt), iw,
-          lane);
-
-  // Top of iteration k (PV and loader waves): wait for this wave's share of
-  // the tile the QK waves start now; the barrier that follows publishes it.
-  // Loads complete in issue order, so the wait allows this wave's loads of
-  // every tile issued after it to stay in flight: its share of the later
-  // first-burst tiles, and (loader waves) of the later tiles issued so far
-  // (kAhead .. k - 1 + kAhead).
-  // Iteration 0 of the pipelined loop reads tiles 0 and 1, so a split of one
-  // tile still waits for tile 0 there.
-  auto wait_tile_loads = [&](int k) {
-    int need = kPipe ? k + 1 : k;
-    if (need >= ntiles) {
-      if (!(kPipe && k == 0)) return;
-      need = ntiles - 1;
-    }
-    const int last = min(ntiles - 1, k - 1 + kAhead);            // last tile issued before this barrier
-    const int later = ld_role ? max(0, last - kAhead + 1) : 0;   // loader-issued tiles so far
-    if (need < npre)
-      wait_vmcnt_le<31>((npre - need - 1) * InitDma::per(iw) + later * LdDma::per(lw));
-    else if (ld_role)
-      wait_vmcnt_le<31>((last - need) * LdDma::per(lw));
-  };
-  static_assert(3 * DmaCount<kFmtFp8, 8>::kPerWave + 2 * DmaCount<kFmtFp8, 4>::kPerWave <= 31 &&
-                3 * DmaCount<kFmtBf16, 8>::kPerWave <= 31, "vmcnt waits fit the dispatch range");
 
   if (qk_role) {
     // ---------------------------------------------------------------- QK role
-    // Q of the group's 32 heads: 36,864 contiguous bytes, brought into ring
-    // buffer kAhead (first loaded with a tile only after the first loop
+    // Q of the group's 32 heads: 36,864 contiguous bytes, brought into the
+    // end of the tile ring (written with a tile only after the first loop
     // barrier, by when Q has been read) with contiguous 1 KB direct-to-LDS
     // loads, then read in the MFMA layout.  Loading it straight into the
     // layout would touch ~32 cache lines per instruction, and the two token
     // halves would load the same heads twice.
     {
-      constexpr int kQBytes = kHpw * kDqk * 2;
-      static_assert(kQBytes % 1024 == 0 && (kNbuf - (kNbuf - 2)) * kTileBytes >= kQBytes, "Q fits the free buffers");
+      static_assert(kQBytes % 1024 == 0 && kQOff % 1024 == 0 && kQOff >= (kPipe ? 2 : 1) * kTileBytes,
+                    "Q lies in the buffers written only after the first loop barrier");
       const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)vr * kHeads + kHpw * hg) * kDqk);
-      uint8_t* qlds = tiles + (kNbuf - 2) * kTileBytes;
+      uint8_t* qlds = tiles + kQOff;
 #pragma unroll
       for (int j = wave; j < kQBytes / 1024; j += kQkWaves)
         dma16(qsrc + 1024 * j + 16 * lane, (uint32_t)(uintptr_t)(qlds + 1024 * j));
@@ -581,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     lds_barrier();   // the translation barrier (the other waves take it in their branch above); Q has landed
     bf16x8 qraw[18];
     {
-      const uint8_t* qrow = tiles + (kNbuf - 2) * kTileBytes + hloc * (kDqk * 2);
+      const uint8_t* qrow = tiles + kQOff + hloc * (kDqk * 2);
       if constexpr (FMT == kFmtFp8) {
         // latent: 32 dims per lane group per block (4 x 8), rope: 8 dims per chunk
 #pragma unroll
@@ -838,19 +869,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     lds_barrier();
   } else if (ld_role) {
     // ------------------------------------------------------------ loader role
-    // Tile k + kAhead goes out right after the barrier of iteration k; its
-    // sources are read from LDS a tile ahead.
-    TileSrc<FMT, kLdWaves> nsrc{};
-    if (kAhead < ntiles) nsrc = tile_src<FMT, kLdWaves>((const uint64_t LDS_AS*)rowaddr_s, kAhead * kTile, lw, lane);
-#pragma clang loop unroll(disable)
-    for (int k = 0; k <= ntiles; ++k) {
-      wait_tile_loads(k);
-      arrive_barrier();
-      if (k + kAhead < ntiles) {
-        issue_tile<FMT, kLdWaves>(nsrc, tile_lds(k + kAhead), lw, lane);
-        if (k + kAhead + 1 < ntiles)
-          nsrc = tile_src<FMT, kLdWaves>((const uint64_t LDS_AS*)rowaddr_s, (k + kAhead + 1) * kTile, lw, lane);
-      }
+    const uint64_t LDS_AS* ra = (const uint64_t LDS_AS*)rowaddr_s;
+    uint8_t LDS_AS* tl = (uint8_t LDS_AS*)smem;
+    // a split holds 16 / nsplit tiles rounded up, or the remainder: one of these
+    switch (ntiles) {
+      case 16: load_rows_nt<FMT, kPipe, 16>(ra, tl, lw, lane); break;
+      case 8: load_rows_nt<FMT, kPipe, 8>(ra, tl, lw, lane); break;
+      case 6: load_rows_nt<FMT, kPipe, 6>(ra, tl, lw, lane); break;
+      case 4: load_rows_nt<FMT, kPipe, 4>(ra, tl, lw, lane); break;
+      case 3: load_rows_nt<FMT, kPipe, 3>(ra, tl, lw, lane); break;
+      case 2: load_rows_nt<FMT, kPipe, 2>(ra, tl, lw, lane); break;
+      default: load_rows_nt<FMT, kPipe, 1>(ra, tl, lw, lane); break;
     }
     lds_barrier();                    // the QK waves publish each half's max and sum
   } else {
@@ -918,7 +947,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // accumulators are reset.
 #pragma clang loop unroll(disable)
     for (int k = 0; k <= ntiles; ++k) {
-      wait_tile_loads(k);
       arrive_barrier();
       const bool dry = k == 0;
       const int kt = dry ? 0 : k - 1;   // tile accumulated in this iteration

@@ -34,3 +34,10 @@ def upload(w: Workload, device="cuda", pool: torch.Tensor | None = None) -> Devi
     return DeviceInputs(q=t(w.q).view(torch.bfloat16), pool=pool, page_table=t(w.page_table),
                         topk_idx=t(w.topk_idx), ctx_len=t(w.ctx_len), kv_format=w.kv_format,
                         pool_pages=w.pool_pages, scale=float(w.scale))
+
+
+def request_slice(d: DeviceInputs, lo: int, hi: int) -> DeviceInputs:
+    """Requests lo .. hi-1 of `d` as their own batch (views of the same memory,
+    same pool): several disjoint batches can be cut from one input set."""
+    return dataclasses.replace(d, q=d.q[lo:hi], page_table=d.page_table[lo:hi], topk_idx=d.topk_idx[lo:hi],
+                               ctx_len=d.ctx_len[lo:hi])
