@@ -436,11 +436,19 @@ __device__ __forceinline__ void load_rows(const uint64_t LDS_AS* rowaddr_s, uint
 #pragma unroll
     for (int q = 0; q < N; ++q) *reinterpret_cast<u32x4 LDS_AS*>(base + dst[q]) = d[q];
   };
+  // Tiles 0 and 1 go out first; the rest of the first S only after tile 0 is
+  // written, so the first write does not queue behind their issue (which
+  // stalls while the compute unit's memory path is full).
+  constexpr int kPre = NT < (S < 2 ? S : 2) ? NT : (S < 2 ? S : 2);
 #pragma unroll
-  for (int t = 0; t < (NT < S ? NT : S); ++t) load(t, reg[t]);
+  for (int t = 0; t < kPre; ++t) load(t, reg[t]);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     write(t, reg[t % S]);
+    if (t == 0) {
+#pragma unroll
+      for (int u = kPre; u < (NT < S ? NT : S); ++u) load(u, reg[u]);
+    }
     if (t + S < NT) load(t + S, reg[t % S]);
     if (!PIPE || t > 0) lds_barrier();
   }
