@@ -541,16 +541,32 @@ def main() -> int:
         if args.selector_sweep:
             t4 = time.time()
             selector = {}
-            for Bs in SWEEP_B:
+            # query tokens per request 2: Q of the extra token drawn per layer
+            q2 = [torch.from_numpy(W.with_query_tokens(w, 2).q).to(dev).view(torch.bfloat16) for w in full]
+            for T, Bs in [(1, b) for b in SWEEP_B] + [(2, b) for b in SWEEP_B]:
                 ins, _ = batches(Bs)
-                shp = smla.make_shape(Bs, full[0].kv_format, full[0].max_pages, base)
-                o = torch.empty((Bs, 64, 512), dtype=torch.bfloat16, device=dev)
-                l_ = torch.empty((Bs, 64), dtype=torch.float32, device=dev)
+                if T == 2:
+                    ins = [(d, q2[i // (full[0].B // Bs)][(i % (full[0].B // Bs)) * Bs:(i % (full[0].B // Bs) + 1) * Bs])
+                           for i, d in enumerate(ins)]
+                shp = smla.make_shape(Bs, full[0].kv_format, full[0].max_pages, base, T)
+                lead = (Bs, T) if T > 1 else (Bs,)
+                o = torch.empty(lead + (64, 512), dtype=torch.bfloat16, device=dev)
+                l_ = torch.empty(lead + (64,), dtype=torch.float32, device=dev)
+
+                def run_one(x, pl, w_s):
+                    if T == 1:
+                        decode(x, shp, pl, w_s, o, l_)
+                        return
+                    d, q_ = x
+                    rc = smla.decode_raw(q_, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, o, l_, shp, pl,
+                                         w_s, stream=stream)
+                    if rc != 0:
+                        raise RuntimeError(f"decode failed: {smla.strerror(rc)}")
 
                 def time_plan(pl):
                     p_, wsb = smla.plan_for(shp, pl)
                     w_s = smla.new_workspace(wsb, dev)
-                    pstep = rotation(ins, lambda d: decode(d, shp, pl, w_s, o, l_))
+                    pstep = rotation(ins, lambda x: run_one(x, pl, w_s))
                     warm(pstep, len(ins), 0.03)
                     return p_, statistics.median(timed(pstep, max(args.sweep_steps, len(ins) // 4))
                                                  for _ in range(3))
@@ -565,9 +581,10 @@ def main() -> int:
                         p_, us = time_plan({"nsplit": ns, "merge": merge})
                         table[label(p_)] = round(us, 2)
                 best = min(table, key=table.get)
-                selector[str(Bs)] = {"pick": label(pick), "pick_us": round(pick_us, 2), "best": best,
-                                     "best_us": table[best], "pick_over_best": round(pick_us / table[best], 3),
-                                     "all_us": table}
+                selector[str(Bs) if T == 1 else f"{Bs}_q{T}"] = {
+                    "pick": label(pick), "pick_us": round(pick_us, 2), "best": best, "best_us": table[best],
+                    "pick_over_best": round(pick_us / table[best], 3), "all_us": table}
+            del q2
             log(f"selector sweep done in {time.time() - t4:.1f}s: "
                 f"{ {b: (v['pick'], v['best'], v['pick_over_best']) for b, v in selector.items()} }")
         del dfull, spool
