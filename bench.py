@@ -36,6 +36,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -65,11 +66,21 @@ DTYPE = {0: "bf16 QK and PV MFMA (bf16 rows), fp32 accumulate",
             "fp32 accumulate"}
 
 
+def code_only(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string
+    literals in these files hold no comment markers)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
+    """First 16 hex digits of sha256 over the code (not the comments) of the
+    split kernel's sources: counters stay valid across comment-only edits."""
     h = hashlib.sha256()
     for f in ("smla_kernels.hip", "smla_internal.h"):
-        with open(os.path.join(ROOT, "sparse_mla_top_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparse_mla_top_amd", "csrc", f)) as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,17 +1,20 @@
 // smla_kernels.hip -- gfx950 kernels of the sparse-MLA decode path.
 //
-//   split kernel   : per (request, top-k split): translate top-k indices to cache
-//                    slots, gather the selected rows into LDS with direct-to-LDS
-//                    loads, QK^T and PV on bf16 MFMA, online softmax, and write a
+//   split kernel   : per (request, head group of 32, top-k split): translate
+//                    top-k indices to cache slots, gather the selected rows into
+//                    LDS (register-staged loads), QK^T on fp8 MFMA (cache codes
+//                    against Q as fp8 hi + lo; bf16 MFMA for the rope and for
+//                    bf16 rows), online softmax, PV on bf16 MFMA, and write a
 //                    normalised partial (O, lse) -- or the final output when the
-//                    request is not split.
+//                    request is not split; optionally the last split merges.
 //   combine kernel : log-sum-exp merge of the partials of each (request, head).
 //   gather kernel  : the translation + gather stage alone (test hook).
 //
 // The split-K structure and the online-softmax merge follow "The 64-Block
 // Barrier" (section "The Split-K Prescription") and "The Commit That Rewrote
 // the Bottleneck" (section "The Levers"); the tiling below is designed for
-// CDNA4 (64-wide waves, 16x16x32 bf16 MFMA, 160 KiB LDS, LDS transpose reads).
+// CDNA4 (64-wide waves, 16x16x128 fp8 and 32x32x16 bf16 MFMA, 160 KiB LDS, LDS
+// transpose reads).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -466,30 +469,34 @@ __device__ __forceinline__ void load_rows_nt(const uint64_t LDS_AS* rowaddr_s, u
 }
 
 // ----------------------------------------------------------------------------
-// Split kernel.  512 threads = 8 waves, one workgroup per (request, split),
-// with two roles that run side by side on each SIMD (waves w and w+4 share
-// SIMD w):
+// Split kernel.  768 threads = 12 waves, one workgroup per (request, head
+// group of 32 heads, split), in three roles; wave w runs on SIMD w % 4:
 //
-//   QK waves 0..3 own heads 16w..16w+15 and every score dim:
-//     S^T[16 tok][16 heads] per 16-token half of a 32-token tile.
+//   QK waves 0..3 own heads 16(w&1)..+15 of the group and token half w>>1 of
+//     every 32-token tile: S^T[16 tok][16 heads].
 //     fp8 rows: per 128-dim scale block one 16x16x128 fp8 MFMA on the cache
-//     codes as stored, against Q split exactly into fp8 hi + lo parts
-//     (Q * 2^e_h = hi + lo, e_h a per-head power of two); the block scale
-//     multiplies the fp32 block partial; the 64 rope dims use 16x16x32 bf16
-//     MFMA.  bf16 rows: 18 bf16 MFMA.  In both operands k-slot g of a block
-//     covers dims 32g..32g+31, so the products pair the same dims.
-//     Online softmax in the log2 domain per head (lane column); the running
-//     max is only raised when a tile's max exceeds it by more than 2^8, so
-//     the output is rarely rescaled (p stays <= 2^8).  P^T goes to LDS, one
-//     bf16 copy per scale block with that block's scales folded in.
+//     codes as stored, against Q * 2^e_h split into fp8 hi + lo parts (e_h the
+//     per-head power of two that puts max|q| in (224, 448]); hi + lo
+//     reproduces Q * 2^e_h except where the residual falls below the e4m3
+//     normal range, which rounds it to the 2^-9 subnormal step (error <= 2^-10
+//     scaled, < 4.4e-6 of the head's max |q|).  The block scale multiplies the
+//     fp32 block partial; the 64 rope dims use 16x16x32 bf16 MFMA.  bf16 rows:
+//     18 bf16 MFMA.  In both operands k-slot g of a block covers dims
+//     32g..32g+31, so the products pair the same dims.
+//     Online softmax in the log2 domain per head (lane column) and half; the
+//     running max is only raised when a tile's max exceeds it by more than
+//     2^8, so the output is rarely rescaled (p stays <= 2^8).  P^T goes to LDS,
+//     one bf16 copy per scale block with that block's scales folded in.
 //   PV waves 4..7 own latent dims 128v..128v+127 (scale block v = w-4) for
-//     all 64 heads: O^T[16 d][16 heads] += V^T[16 d][32 tok] . P^T[32 tok][16 h]
-//     with V^T from one ds_read_tr8_b64 (fp8, converted exactly to bf16) or
-//     two ds_read_tr16_b64 (bf16) per 16-dim tile.
+//     the group's 32 heads: O^T[32 d][32 heads] += V^T[32 d][16 tok] .
+//     P^T[16 tok][32 heads] per token half, with V^T from ds_read_tr8_b64
+//     (fp8, converted exactly to bf16) or ds_read_tr16_b64 (bf16).
+//   Loader waves 8..11 move the rows (load_rows).  PV and loader waves first
+//     translate the split's top-k indices, one token per thread.
 //
-// Iteration k of the shared loop: QK waves score tile k while PV waves
-// accumulate tile k-1; one workgroup barrier per iteration.  Rows stream into a
-// ring of kNbuf LDS tile buffers with direct-to-LDS loads issued ahead.
+// Iteration k of the shared loop: QK waves finish tile k and start tile k+1
+// while PV waves accumulate tile k-1; one workgroup barrier per iteration.
+// Rows sit in a ring of kNbuf LDS tile buffers, written by the loader waves.
 // k-slot i of lane group g holds token tok(g,i) = (i<4) ? 4g+i : 16+4g+i-4,
 // which is where the S^T accumulators of the two halves hold them.
 template <int FMT>
