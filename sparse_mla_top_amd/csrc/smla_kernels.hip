@@ -765,7 +765,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       for (int i = 0; i < 4; ++i) sv[i] = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
     };
     // softmax of tile kt from its raw scores; P^T and alpha to LDS
-    auto finish_tile = [&](int kt, bool dry, const Raw& r, const float4 (&sv)[4], uint32_t vmask) {
+    auto finish_tile = [&](int kt, const Raw& r, const float4 (&sv)[4], uint32_t vmask) {
       f32x4 sacc = r.sm;
       if constexpr (FMT == kFmtFp8) {
 #pragma unroll
@@ -783,7 +783,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         tmax = fmaxf(tmax, v);
       }
       tmax = wave_max16(tmax);
-      float m_cur = dry ? -INFINITY : m_run;
+      float m_cur = m_run;
       float alpha = 1.0f;
       if (__builtin_amdgcn_ballot_w64(tmax > m_cur + 8.0f)) {
         const float m_new = (tmax > m_cur + 8.0f) ? tmax : m_cur;
@@ -797,10 +797,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         p[i] = __builtin_amdgcn_exp2f(p[i] - m_use);
         psum += p[i];
       }
-      if (!dry) {
-        m_run = m_cur;
-        l_run = l_run * alpha + psum;
-      }
+      m_run = m_cur;
+      l_run = l_run * alpha + psum;
       // P^T row of this head and half, tokens 4g .. 4g+3, one bf16 copy per
       // scale block with the block's scale folded in (the PV operand as is)
       const int pb = kt & 1;
@@ -813,23 +811,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       }
       if (g == 0) alpha_s[pb][mh][hloc] = alpha;
     };
-    // One iteration: k = -1 is a warm-up pass through the same code on
-    // whatever buffer 0 holds, every slot masked and its state thrown away,
-    // which pulls the loop's instructions into the instruction cache while the
-    // first tiles are in flight (its P/alpha writes land in buffer 0, which
-    // iteration 0 overwrites before any PV wave reads it).  Iteration k >= 0
-    // finishes tile k (scores in `cur`) and starts tile k+1 (into `nxt`).
+    // Iteration k finishes tile k (raw scores in `cur`) and starts tile k+1
+    // (into `nxt`), between barriers k and k+1.
     auto body = [&](int k, Raw& cur, Raw& nxt) {
-      const bool dry = k < 0;
       if constexpr (kPipe) {   // (the bf16 ring runs the unpipelined loop below)
-        if (k <= 0) {
-          if (!dry) lds_barrier();
+        if (k == 0) {
+          lds_barrier();
           issue_scores(0, cur);
         }
-        const int kt = dry ? 0 : k;
         float4 sv[4];
-        read_scales(kt, sv);
-        const uint32_t mask = mask_s[kt];
+        read_scales(k, sv);
+        const uint32_t mask = mask_s[k];
         // The K reads and MFMAs of tile k+1 are unconditional so the compiler
         // can count the LDS reads in flight and let the softmax wait for the
         // scales alone; after the last tile they read a stale buffer and the
@@ -837,32 +829,29 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         KOps ko;
         read_k(k + 1, ko);
         __builtin_amdgcn_sched_barrier(0);   // every read goes out before the softmax waits
-        finish_tile(kt, dry, cur, sv, dry ? 0u : mask);
+        finish_tile(k, cur, sv, mask);
         mfma_scores(ko, nxt);
-        if (!dry) lds_barrier();
+        lds_barrier();
       }
     };
     Raw ra;   // one buffer: tile k's raw scores are consumed before tile k+1's MFMAs overwrite them
-    const int kfirst = __builtin_amdgcn_readfirstlane(a.nsplit > 0 ? -1 : 0);
     if constexpr (kPipe) {
-      // unrolled by two so the raw scores alternate between ra and rb
+      // unrolled by two
 #pragma clang loop unroll(disable)
-      for (int k = kfirst; k < ntiles; k += 2) {
+      for (int k = 0; k < ntiles; k += 2) {
         body(k, ra, ra);
         if (k + 1 < ntiles) body(k + 1, ra, ra);
       }
     } else {
 #pragma clang loop unroll(disable)
-      for (int k = kfirst; k <= ntiles; ++k) {
-        const bool dry = k < 0;
-        if (!dry) lds_barrier();
+      for (int k = 0; k <= ntiles; ++k) {
+        lds_barrier();
         if (k == ntiles) break;
         Raw r;
-        const int kt = dry ? 0 : k;
-        issue_scores(kt, r);
+        issue_scores(k, r);
         float4 sv[4];
-        if constexpr (FMT == kFmtFp8) read_scales(kt, sv);
-        finish_tile(kt, dry, r, sv, dry ? 0u : mask_s[kt]);
+        if constexpr (FMT == kFmtFp8) read_scales(k, sv);
+        finish_tile(k, r, sv, mask_s[k]);
       }
     }
 
