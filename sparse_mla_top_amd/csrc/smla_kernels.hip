@@ -518,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
   uint8_t* const tiles = smem;
   __shared__ uint64_t rowaddr_s[kTopk];            // row address | 1 when masked
-  __shared__ uint32_t mask_s[kTiles];              // bit t: token t of the tile is valid
+  __shared__ __attribute__((aligned(16))) float bias_s[kTopk];   // score bias of each slot: 0 valid, -inf masked
   // P^T in bf16, already multiplied by the token's scale of the copy's block:
   // [buffer][copy][16-token half][head][token]
   __bf16 (*const p_s)[kPCopies][2][kHpw][kPRow] =
@@ -572,7 +572,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
   // so Q streams in during the two dependent index loads instead of sharing
   // the compute unit's memory path with the first tiles.
   if (!qk_role) {
-    const int tw = wave - kQkWaves;                 // translating wave 0 .. 7
     const int t = threadIdx.x - 64 * kQkWaves;      // token 0 .. 511
     bool valid = false;
     if (t < ntok) {
@@ -581,11 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       valid = slot >= 0;
       rowaddr_s[t] = valid ? (uint64_t)(uintptr_t)(a.pool + slot * kRow)
                            : ((uint64_t)(uintptr_t)g_zero_row | 1ull);
-    }
-    const uint64_t bits = __builtin_amdgcn_ballot_w64(valid);
-    if (lane == 0 && 2 * tw < kTiles) {
-      mask_s[2 * tw] = (uint32_t)bits;
-      mask_s[2 * tw + 1] = (uint32_t)(bits >> 32);
+      bias_s[t] = valid ? 0.f : -INFINITY;
     }
     lds_barrier();   // the QK waves take the same barrier in their own branch below
   }
@@ -765,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       for (int i = 0; i < 4; ++i) sv[i] = *reinterpret_cast<const float4*>(tb + TL::off(16 * mh + 4 * g + i, kDl / 16));
     };
     // softmax of tile kt from its raw scores; P^T and alpha to LDS
-    auto finish_tile = [&](int kt, const Raw& r, const float4 (&sv)[4], uint32_t vmask) {
+    auto finish_tile = [&](int kt, const Raw& r, const float4 (&sv)[4], const float4& bias) {
       f32x4 sacc = r.sm;
       if constexpr (FMT == kFmtFp8) {
 #pragma unroll
@@ -777,8 +772,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
       float tmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = (vmask >> (16 * mh + 4 * g + i)) & 1u;
-        const float v = ok ? sacc[i] * sc_log2 : -INFINITY;
+        const float v = __builtin_fmaf(sacc[i], sc_log2, (&bias.x)[i]);   // -inf when masked
         p[i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -821,7 +815,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         }
         float4 sv[4];
         read_scales(k, sv);
-        const uint32_t mask = mask_s[k];
+        const float4 bias = *reinterpret_cast<const float4*>(&bias_s[k * kTile + 16 * mh + 4 * g]);
         // The K reads and MFMAs of tile k+1 are unconditional so the compiler
         // can count the LDS reads in flight and let the softmax wait for the
         // scales alone; after the last tile they read a stale buffer and the
@@ -829,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         KOps ko;
         read_k(k + 1, ko);
         __builtin_amdgcn_sched_barrier(0);   // every read goes out before the softmax waits
-        finish_tile(k, cur, sv, mask);
+        finish_tile(k, cur, sv, bias);
         mfma_scores(ko, nxt);
         lds_barrier();
       }
@@ -851,7 +845,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         issue_scores(k, r);
         float4 sv[4];
         if constexpr (FMT == kFmtFp8) read_scales(k, sv);
-        finish_tile(k, r, sv, mask_s[k]);
+        finish_tile(k, r, sv, *reinterpret_cast<const float4*>(&bias_s[k * kTile + 16 * mh + 4 * g]));
       }
     }
 
