@@ -154,6 +154,8 @@ def main() -> int:
     ap.add_argument("--no-mtp", action="store_true", help="skip the several-query-tokens pass")
     ap.add_argument("--no-append", action="store_true", help="skip the cache-producer pass")
     ap.add_argument("--no-indexer", action="store_true", help="skip the top-k indexer pass")
+    ap.add_argument("--no-row-read", action="store_true",
+                    help="skip timing the headline's selected rows read alone (smla_read_rows)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other standard workloads (B=1 bf16, B=32, B=96 ragged)")
@@ -285,6 +287,58 @@ def main() -> int:
         else:
             traffic = t.get("hbm_bytes_per_launch")
             traffic_note = t.get("note", "")
+
+    # ------------------------------------------------------------------ row reads alone
+    # The headline's selected rows read by smla_read_rows, which brings them
+    # into the compute units and discards them (no translation, Q, arithmetic
+    # or output): (a) as the decode reads them, one group of 512 rows per
+    # (request, head group), one compute unit each, the two groups of a request
+    # 8 block indices apart so they run on one XCD as the decode's do; (b) every
+    # row once, spread over all compute units.  (a) is the floor of the decode's
+    # own data movement, (b) that of any decomposition that reads each row once.
+    row_read = None
+    if not args.no_row_read:
+        t3 = time.time()
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        slot_sets = []
+        for w, d in sets:
+            _, sl = smla.gather_rows(d.pool, d.page_table, d.topk_idx, d.ctx_len, kv_format=w.kv_format,
+                                     pool_pages=pool_pages)
+            slot_sets.append(sl)
+        torch.cuda.synchronize()
+        order = []
+        for c0 in range(0, B, 8):
+            rs = list(range(c0, min(B, c0 + 8)))
+            order += rs + rs
+        order = torch.tensor(order, dtype=torch.long, device=dev)
+        valid_rows = float(np.mean([int((sl >= 0).sum()) for sl in slot_sets]))
+        row_read = {}
+        for name in ("decode_layout", "each_row_once"):
+            if name == "decode_layout":
+                lists = [sl[order].reshape(-1).contiguous() for sl in slot_sets]
+                per, groups, n_rows = 512, 2 * B, 2 * valid_rows
+            else:
+                lists = [sl.reshape(-1).contiguous() for sl in slot_sets]
+                per = -(-lists[0].numel() // n_cu)
+                groups, n_rows = -(-lists[0].numel() // per), valid_rows
+            sink = torch.empty(groups * 1024, dtype=torch.int32, device=dev)
+
+            def read(lst, per=per, groups=groups, sink=sink):
+                rc = smla.read_rows_raw(pool, pool_pages * W.PAGE, lst, per, w0.row_bytes, groups, sink, stream)
+                if rc != 0:
+                    raise RuntimeError(f"read_rows failed: {smla.strerror(rc)}")
+            rstep = rotation(lists, read)
+            warm(rstep, max(args.warmup, L))
+            rst = repeat_stats([timed(rstep, args.steps) for _ in range(3)])
+            byts = n_rows * w0.row_bytes
+            gbs = byts / (rst["median_us"] * 1e-6) / 1e9
+            row_read[name] = {"groups": groups, "rows_per_group": per, "us": rst["median_us"],
+                              "spread": rst["spread"], "row_bytes_per_call": int(byts), "GBps": round(gbs, 1),
+                              "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                              "frac_of_device_copy": round(gbs / copy_gbs, 4)}
+        del slot_sets
+        log(f"row reads alone done in {time.time() - t3:.1f}s: "
+            f"{ {k: (v['us'], v['GBps'], v['groups']) for k, v in row_read.items()} }")
 
     # ------------------------------------------------------------------ query tokens
     # q_len query tokens per request sharing its selection, on the headline
@@ -651,6 +705,7 @@ def main() -> int:
             "roofline_us_per_call": round(roof_us, 3),
             "mfma": mfma_report(call_cost, full_us, w0.kv_format),
             "traffic_note": traffic_note,
+            "row_read": row_read,
             "sweep": sweep,
             "indexer_topk": indexer,
             "selector_check": selector,
@@ -667,7 +722,9 @@ def main() -> int:
         "roofline": {"kernel": KERNEL_NAME, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "device_copy_GBps": round(copy_gbs, 1),
-                     "frac_of_device_copy": round(achieved / copy_gbs, 4)},
+                     "frac_of_device_copy": round(achieved / copy_gbs, 4),
+                     "row_read_floor_us": None if row_read is None else row_read["decode_layout"]["us"],
+                     "row_read_once_us": None if row_read is None else row_read["each_row_once"]["us"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

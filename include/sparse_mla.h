@@ -264,6 +264,27 @@ int smla_gather_rows(const void* kv_pool, const int32_t* page_table, const int32
                      void* stream);
 
 /*
+ * smla_read_rows -- measurement aid: reads cache rows and discards them, so the
+ * rate at which this device can move the rows the decode reads can be measured
+ * with nothing else done to them (the pages judge the decode against the memory
+ * bandwidth it reaches on scattered FP8 row gathers: "Inside the Decode
+ * Performance Investigation", section "Task 1").
+ *   kv_pool   [device] u8 pool of pool_rows >= 1 rows of row_bytes bytes, 16-byte aligned
+ *   slots     [device] i64 [n_slots]: row indices (as smla_gather_rows returns);
+ *             -1 and indices outside [0, pool_rows) are skipped
+ *   per_group, n_groups: workgroup g (one per compute unit) reads the rows of
+ *             slots[g * per_group .. + per_group); per_group <= 4096,
+ *             n_groups * per_group >= n_slots
+ *   row_bytes 656 or 1152
+ *   sink      [device] u32 [n_groups * 1024]: per thread, the XOR of the four
+ *             words of every 16-byte piece it read (thread t of group g reads
+ *             pieces t, t + 1024, ... of the group's rows laid end to end)
+ * Asynchronous on `stream`; returns SMLA_OK, SMLA_ERR_INVALID_ARG or SMLA_ERR_HIP.
+ */
+int smla_read_rows(const void* kv_pool, int64_t pool_rows, const int64_t* slots, int64_t n_slots,
+                   int32_t per_group, int32_t row_bytes, int32_t n_groups, uint32_t* sink, void* stream);
+
+/*
  * smla_kv_append -- the cache producer: quantise n_tokens new tokens' rows and
  * write them into the paged cache in the row format this library reads (the
  * pages name the FP8 latent cache the decode gathers from, "Inside the Decode

@@ -91,6 +91,9 @@ def lib():
         L.smla_workspace_init.restype = ctypes.c_int
         L.smla_gather_rows.argtypes = [vp, i32p, i32p, i32p, ctypes.POINTER(Shape), vp, i64p, vp]
         L.smla_gather_rows.restype = ctypes.c_int
+        L.smla_read_rows.argtypes = [vp, ctypes.c_int64, i64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, vp, vp]
+        L.smla_read_rows.restype = ctypes.c_int
         L.smla_kv_append.argtypes = [vp, vp, i32p, i32p, i32p, vp, ctypes.c_int32, ctypes.POINTER(Shape), vp]
         L.smla_kv_append.restype = ctypes.c_int
         L.smla_indexer_topk.argtypes = [vp, vp, vp, i32p, i32p, vp, i32p, ctypes.POINTER(Shape), vp]
@@ -264,6 +267,18 @@ def gather_rows(kv_pool, page_table, topk_idx, ctx_len, *, kv_format: int, pool_
     if rc != OK:
         raise SmlaError(rc, "smla_gather_rows")
     return rows, slots
+
+
+def read_rows_raw(kv_pool, pool_rows: int, slots, per_group: int, row_bytes: int, n_groups: int, sink,
+                  stream=None) -> int:
+    """smla_read_rows on torch tensors (slots int64, sink uint32-sized int32); returns the status code."""
+    n = int(slots.numel())
+    for t, nbytes, name in ((slots, n * 8, "slots"), (sink, int(n_groups) * 1024 * 4, "sink"),
+                            (kv_pool, int(pool_rows) * int(row_bytes), "kv_pool")):
+        if t.numel() * t.element_size() < nbytes or not t.is_contiguous():
+            raise ValueError(f"{name}: smaller than the call needs ({nbytes} bytes) or not contiguous")
+    return lib().smla_read_rows(_ptr(kv_pool), int(pool_rows), _ptr(slots), n, int(per_group), int(row_bytes),
+                                int(n_groups), _ptr(sink), _stream(stream))
 
 
 def kv_append_raw(latent, rope, req, pos, page_table, kv_pool, shape: Shape, stream=None) -> int:

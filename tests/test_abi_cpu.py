@@ -204,3 +204,23 @@ def test_in_kernel_merge_limited_to_counter_head():
         assert p.merge == smla.MERGE_SEPARATE
         with pytest.raises(smla.SmlaError):
             smla.plan_for_cus(_shape(batch=B, q_len=q), 256, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL})
+
+
+def test_read_rows_validation():
+    """smla_read_rows rejects bad arguments before touching the device."""
+    L = smla.lib()
+    p = ctypes.c_void_p(256)
+    rr = L.smla_read_rows
+    assert rr(None, 100, p, 10, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG
+    assert rr(p, 100, None, 10, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG
+    assert rr(p, 100, p, 10, 10, 656, 1, None, None) == smla.ERR_INVALID_ARG
+    assert rr(p, -1, p, 10, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG
+    assert rr(p, 0, p, 10, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG       # empty pool
+    assert rr(p, 100, p, 10, 4097, 656, 1, p, None) == smla.ERR_INVALID_ARG   # group beyond the staged offsets
+    assert rr(p, 100, p, -1, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG
+    assert rr(p, 100, p, 10, 0, 656, 1, p, None) == smla.ERR_INVALID_ARG
+    assert rr(p, 100, p, 10, 10, 640, 1, p, None) == smla.ERR_INVALID_ARG     # not a row size of this library
+    assert rr(ctypes.c_void_p(264), 100, p, 10, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG   # pool unaligned
+    assert rr(p, 100, ctypes.c_void_p(260), 10, 10, 656, 1, p, None) == smla.ERR_INVALID_ARG   # slots unaligned
+    assert rr(p, 100, p, 10, 4, 656, 2, p, None) == smla.ERR_INVALID_ARG      # 2 groups of 4 cannot cover 10 slots
+    assert rr(p, 100, p, 0, 4, 1152, 0, p, None) == smla.OK                    # nothing to read
