@@ -91,16 +91,18 @@ size_t workspace_for(int B, int nsplit) {
 // kernel, one workgroup per request reads every partial (bounded by one CU's
 // memory parallelism); as a separate launch, a launch gap plus a short,
 // device-wide read.  The constants are fitted to MI355X timings on cold
-// caches (B = 1..80, nsplit = 1..8, both merges).
+// caches (B = 1..96 with one and two query tokens, every split count and both
+// merges), chosen so that the pick is the measured best or within a few per
+// cent of it at every batch size.
 double est_time_us(int B, int q_len, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
-  const double t_start = 7.0;        // launch, translation and first-gather latency per workgroup
-  const double us_per_mb_burst = 0.1;   // first tiles and Q of every resident workgroup
-  const double t_tile = 0.9;         // one 32-token tile for 32 heads on one CU
-  const double t_per_split = 0.4;    // per split of a request, within a round
-  const double us_per_mb = 0.03;     // gathered rows and per-split Q reads, device-wide
-  const double t_fused0 = 3.5, t_fused_split = 0.6;   // in-kernel merge: one workgroup reads every partial
-  const double t_sep0 = 2.0, t_sep_split = 0.1;       // combine launch: gap, lse, partial rounds
-  const double us_per_mb_part = 0.2;                  // partial bytes written and read back
+  const double t_start = 6.26;       // launch, translation and first-gather latency per workgroup
+  const double us_per_mb_burst = 0.091;  // first tiles and Q of every resident workgroup
+  const double t_tile = 0.566;        // one 32-token tile for 32 heads on one CU
+  const double t_per_split = 0.139;   // per split of a request, within a round
+  const double us_per_mb = 0.0749;    // gathered rows and per-split Q reads, device-wide
+  const double t_fused0 = 5.10, t_fused_split = 0.567;   // in-kernel merge: one workgroup reads every partial
+  const double t_sep0 = 2.63, t_sep_split = 0.0749;      // combine launch: gap, lse, partial rounds
+  const double us_per_mb_part = 0.1253;                 // partial bytes written and read back
   const double mb = 1.0 / (1 << 20);
   const int grid = B * q_len * kHeadGroups * nsplit;
   const int rounds = (grid + cus - 1) / cus;
