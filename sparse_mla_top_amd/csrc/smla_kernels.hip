@@ -1093,30 +1093,33 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Combine as a launch of its own, spread over the device: one 256-thread
-// workgroup per (request, latent slice vb, 32-head block hb); wave w merges
-// the four runs (vb, db = w, jj, hb).  Weights come from split_weights and the
-// runs are accumulated in split order, exactly as the fused merge does, so
-// both give identical bits.
-constexpr int kCombineThreads = 256;
+// Combine as a launch of its own, spread over the device: one single-wave
+// workgroup per (query set, latent slice vb, 32-head block hb, 32-dim block
+// db), which merges the four runs (vb, db, jj, hb), so a query set's partials
+// are read through 32 compute units.  Every split's runs are requested before
+// the weights are known, up to kCombineBatch splits at once.  Weights come from
+// split_weights and the runs are accumulated in split order, exactly as the
+// fused merge does, so both give identical bits.
+constexpr int kCombineThreads = 64;
+constexpr int kCombineBatch = 8;
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a) {
   __shared__ float wt[16 * 32];
-  const int b = blockIdx.x >> 3, vb = (blockIdx.x >> 1) & 3, hb = blockIdx.x & 1;
-  const int t = threadIdx.x, db = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
+  const int b = blockIdx.x >> 5, vb = (blockIdx.x >> 3) & 3, hb = (blockIdx.x >> 2) & 1, db = blockIdx.x & 3;
+  const int lane = threadIdx.x, l32 = lane & 31, kg = lane >> 5;
   const int ns = a.nsplit;
   const float* ls = a.part_lse + (int64_t)b * ns * kHeads + 32 * hb;
-  // the lse loads (two per thread at most) and the first four partials go
-  // out together: the weights are computed while the runs are in flight
-  float lv[2];
+  // the lse loads (at most 8 per lane) and the first batch of runs go out
+  // together: the weights are computed while the runs are in flight
+  float lv[8];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = t + u * kCombineThreads;
+  for (int u = 0; u < 8; ++u) {
+    const int i = lane + u * kCombineThreads;
     lv[u] = i < ns * 32 ? load_agent(ls + (i >> 5) * kHeads + (i & 31)) : 0.f;
   }
-  f32x4 v[4][4];
+  f32x4 v[kCombineBatch][4];
   auto issue = [&](int sp) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kCombineBatch; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         v[u][j] = sp + u < ns ? load_run(a.part_o, (int64_t)b * ns + sp + u, part_run_offset(vb, db, j, hb, lane))
@@ -1124,21 +1127,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(CombineArgs a)
   };
   issue(0);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-    if (t + u * kCombineThreads < ns * 32) wt[t + u * kCombineThreads] = lv[u];
+  for (int u = 0; u < 8; ++u)
+    if (lane + u * kCombineThreads < ns * 32) wt[lane + u * kCombineThreads] = lv[u];
   __syncthreads();
-  if (t < 32) {   // in place, column t: the lse of head 32hb + t
-    const float l = split_weights(ns, [&](int sp) { return wt[sp * 32 + t]; }, wt + t, 32);
-    if (vb == 0) a.lse[(int64_t)b * kHeads + 32 * hb + t] = l;
+  if (lane < 32) {   // in place, column lane: the lse of head 32hb + lane
+    const float l = split_weights(ns, [&](int sp) { return wt[sp * 32 + lane]; }, wt + lane, 32);
+    if (vb == 0 && db == 0) a.lse[(int64_t)b * kHeads + 32 * hb + lane] = l;
   }
   __syncthreads();
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < ns; sp += 4) {
+  for (int sp = 0; sp < ns; sp += kCombineBatch) {
     if (sp > 0) issue(sp);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kCombineBatch; ++u) {
       if (sp + u >= ns) break;
       const float w = wt[(sp + u) * 32 + l32];
 #pragma unroll
@@ -1189,7 +1192,7 @@ hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t st
 }
 
 hipError_t launch_combine(const CombineArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(B * 8), dim3(kCombineThreads), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(B * 32), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 
