@@ -293,9 +293,11 @@ def main() -> int:
     # into the compute units and discards them (no translation, Q, arithmetic
     # or output): (a) as the decode reads them, one group of 512 rows per
     # (request, head group), one compute unit each, the two groups of a request
-    # 8 block indices apart so they run on one XCD as the decode's do; (b) every
-    # row once, spread over all compute units.  (a) is the floor of the decode's
-    # own data movement, (b) that of any decomposition that reads each row once.
+    # 8 block indices apart so they run on one XCD as the decode's do; (b) each
+    # request's rows once, one compute unit per request (a 64-head workgroup's
+    # movement, unsplit); (c) every row once, spread over all compute units.
+    # (a) is the floor of the decode's own data movement, (c) that of any
+    # decomposition that reads each row once.
     row_read = None
     if not args.no_row_read:
         t3 = time.time()
@@ -313,10 +315,13 @@ def main() -> int:
         order = torch.tensor(order, dtype=torch.long, device=dev)
         valid_rows = float(np.mean([int((sl >= 0).sum()) for sl in slot_sets]))
         row_read = {}
-        for name in ("decode_layout", "each_row_once"):
+        for name in ("decode_layout", "request_once", "each_row_once"):
             if name == "decode_layout":
                 lists = [sl[order].reshape(-1).contiguous() for sl in slot_sets]
                 per, groups, n_rows = 512, 2 * B, 2 * valid_rows
+            elif name == "request_once":
+                lists = [sl.reshape(-1).contiguous() for sl in slot_sets]
+                per, groups, n_rows = 512, B, valid_rows
             else:
                 lists = [sl.reshape(-1).contiguous() for sl in slot_sets]
                 per = -(-lists[0].numel() // n_cu)
