@@ -297,7 +297,10 @@ def main() -> int:
     # request's rows once, one compute unit per request (a 64-head workgroup's
     # movement, unsplit); (c) every row once, spread over all compute units.
     # (a) is the floor of the decode's own data movement, (c) that of any
-    # decomposition that reads each row once.
+    # decomposition that reads each row once.  (d) reads the rows of every
+    # input set in one launch over all compute units (16 layers' worth, no
+    # launch or ramp in the way): the sustained rate of this random gather;
+    # (e) the same number of rows, consecutive in the pool, for comparison.
     row_read = None
     if not args.no_row_read:
         t3 = time.time()
@@ -315,17 +318,26 @@ def main() -> int:
         order = torch.tensor(order, dtype=torch.long, device=dev)
         valid_rows = float(np.mean([int((sl >= 0).sum()) for sl in slot_sets]))
         row_read = {}
-        for name in ("decode_layout", "request_once", "each_row_once"):
+        for name in ("decode_layout", "request_once", "each_row_once", "all_sets_once", "all_sets_consecutive"):
             if name == "decode_layout":
                 lists = [sl[order].reshape(-1).contiguous() for sl in slot_sets]
                 per, groups, n_rows = 512, 2 * B, 2 * valid_rows
             elif name == "request_once":
                 lists = [sl.reshape(-1).contiguous() for sl in slot_sets]
                 per, groups, n_rows = 512, B, valid_rows
-            else:
+            elif name == "each_row_once":
                 lists = [sl.reshape(-1).contiguous() for sl in slot_sets]
                 per = -(-lists[0].numel() // n_cu)
                 groups, n_rows = -(-lists[0].numel() // per), valid_rows
+            elif name == "all_sets_once":
+                lists = [torch.cat([sl.reshape(-1) for sl in slot_sets]).contiguous()]
+                per = -(-lists[0].numel() // n_cu)
+                groups, n_rows = -(-lists[0].numel() // per), valid_rows * len(slot_sets)
+            else:
+                n_all = sum(sl.numel() for sl in slot_sets)
+                lists = [torch.arange(n_all, dtype=torch.long, device=dev)]
+                per = -(-n_all // n_cu)
+                groups, n_rows = -(-n_all // per), n_all
             sink = torch.empty(groups * 1024, dtype=torch.int32, device=dev)
 
             def read(lst, per=per, groups=groups, sink=sink):
@@ -611,6 +623,7 @@ def main() -> int:
         if args.selector_sweep:
             t4 = time.time()
             selector = {}
+            n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
             # query tokens per request 2: Q of the extra token drawn per layer
             q2 = [torch.from_numpy(W.with_query_tokens(w, 2).q).to(dev).view(torch.bfloat16) for w in full]
             for T, Bs in [(1, b) for b in SWEEP_B] + [(2, b) for b in SWEEP_B]:
@@ -642,12 +655,16 @@ def main() -> int:
                                                  for _ in range(3))
 
                 def label(p_):
-                    where = {smla.MERGE_IN_KERNEL: "in-kernel", smla.MERGE_SEPARATE: "separate"}.get(p_.merge, "-")
+                    where = {smla.MERGE_IN_KERNEL: "in-kernel", smla.MERGE_SEPARATE: "separate",
+                             smla.MERGE_SPREAD: "spread"}.get(p_.merge, "-")
                     return f"{p_.nsplit}/{where}/h{p_.heads_per_wg}/t{p_.tile_tokens}/wg{p_.wg_per_cu}"
                 pick, pick_us = time_plan(None)
                 table = {}
                 for ns in (1, 2, 3, 4, 6, 8, 16):
-                    for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
+                    merges = (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)
+                    if ns > 1 and Bs * T * 2 * ns <= n_cus:   # the spread merge needs the whole grid resident
+                        merges += (smla.MERGE_SPREAD,)
+                    for merge in merges:
                         p_, us = time_plan({"nsplit": ns, "merge": merge})
                         table[label(p_)] = round(us, 2)
                 best = min(table, key=table.get)

@@ -109,6 +109,12 @@ typedef struct {
                                   the same launch; only for batch * q_len <= 4096 (a plan
                                   forcing it beyond that returns SMLA_ERR_PLAN)            */
 #define SMLA_MERGE_SEPARATE 2  /* a second launch: the combine kernel                      */
+#define SMLA_MERGE_SPREAD 3    /* the same launch: once every split of a request has written
+                                  its partial, each merges an equal share of the dims; only
+                                  when every workgroup of the launch is resident at once
+                                  (batch * q_len * 2 * nsplit <= compute units) and for
+                                  batch * q_len <= 4096 (a plan forcing it otherwise returns
+                                  SMLA_ERR_PLAN)                                           */
 
 /* Launch plan.  Zero fields mean "choose automatically". */
 typedef struct {
@@ -176,9 +182,11 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *                        went wrong).  If it gives up, it sets the status word,
  *                        leaves the counters as they are, still merges what the
  *                        partials hold and writes NaN into lse for that request's
- *                        heads; while the status word is set every call that
- *                        merges in-kernel on the workspace writes NaN into lse and
- *                        leaves out as it was.  A NaN lse therefore
+ *                        heads.  A spread merge (SMLA_MERGE_SPREAD) that gives up
+ *                        sets the same word and writes NaN into lse and into the
+ *                        share of out it merges.  While the status word is set
+ *                        every call that merges in the kernel (either form) on the
+ *                        workspace writes NaN into lse and leaves out as it was.  A NaN lse therefore
  *                        means: call smla_workspace_init before the workspace's
  *                        next use.  In validate mode the call waits and returns
  *                        SMLA_ERR_MERGE when the status word is set.  (The
@@ -188,9 +196,11 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  * With nsplit = 1 the work is one kernel launch.  Otherwise each (request,
  * split) workgroup writes its partial result and the partials are merged by
  * the log-sum-exp combine of "The 64-Block Barrier", section "The Split-K
- * Prescription": either by the last split of each request to finish, in the
- * same launch (SMLA_MERGE_IN_KERNEL), or by the combine kernel launched right
- * after on the same stream (SMLA_MERGE_SEPARATE), as the plan says.
+ * Prescription": by the last split of each request to finish, in the same
+ * launch (SMLA_MERGE_IN_KERNEL); by every split, each merging a share of the
+ * dims once all have written, in the same launch (SMLA_MERGE_SPREAD); or by the
+ * combine kernel launched right after on the same stream (SMLA_MERGE_SEPARATE),
+ * as the plan says.
  * Returns SMLA_OK or a negative SMLA_ERR_* code.
  */
 int sparse_mla_decode(const void* q, const void* kv_pool, const int32_t* page_table,

@@ -37,6 +37,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20   # the workspace that sparse_mla_decode_noallo
 MERGE_AUTO = 0
 MERGE_IN_KERNEL = 1
 MERGE_SEPARATE = 2
+MERGE_SPREAD = 3     # same launch, every split merges a share (grids of at most one workgroup per CU)
 
 
 class Shape(ctypes.Structure):

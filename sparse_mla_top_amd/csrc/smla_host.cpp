@@ -89,20 +89,22 @@ size_t workspace_for(int B, int nsplit) {
 // every resident workgroup fetching its first tiles and its Q at once, a
 // burst whose size grows with the grid.  Splitting adds the merge: in the
 // kernel, one workgroup per request reads every partial (bounded by one CU's
-// memory parallelism); as a separate launch, a launch gap plus a short,
-// device-wide read.  The constants are fitted to MI355X timings on cold
-// caches (B = 1..96 with one and two query tokens, every split count and both
-// merges), chosen so that the pick is the measured best or within a few per
-// cent of it at every batch size.
+// memory parallelism), or every split reads its share after a rendezvous; as a
+// separate launch, a launch gap plus a short, device-wide read.  The constants
+// are fitted to MI355X timings on cold caches (B = 1..96 with one and two
+// query tokens, every split count and every merge placement), chosen so that
+// the pick is the measured best or within a few per cent of it at every batch
+// size.
 double est_time_us(int B, int q_len, int nsplit, int chunk_tiles, int cus, int merge, int row_bytes) {
-  const double t_start = 6.26;       // launch, translation and first-gather latency per workgroup
-  const double us_per_mb_burst = 0.091;  // first tiles and Q of every resident workgroup
-  const double t_tile = 0.566;        // one 32-token tile for 32 heads on one CU
-  const double t_per_split = 0.139;   // per split of a request, within a round
-  const double us_per_mb = 0.0749;    // gathered rows and per-split Q reads, device-wide
-  const double t_fused0 = 5.10, t_fused_split = 0.567;   // in-kernel merge: one workgroup reads every partial
-  const double t_sep0 = 2.63, t_sep_split = 0.0749;      // combine launch: gap, lse, partial rounds
-  const double us_per_mb_part = 0.1253;                 // partial bytes written and read back
+  const double t_start = 3.1863;          // launch, translation and first-gather latency per workgroup
+  const double us_per_mb_burst = 0.0878;  // first tiles and Q of every resident workgroup
+  const double t_tile = 0.7763;           // one 32-token tile for 32 heads on one CU
+  const double t_per_split = 0.0539;      // per split of a request, within a round
+  const double us_per_mb = 0.0915;        // gathered rows and per-split Q reads, device-wide
+  const double t_fused0 = 4.9696, t_fused_split = 1.1186;    // in-kernel merge: one workgroup reads every partial
+  const double t_sep0 = 5.9727, t_sep_split = 0.3295;        // combine launch: gap, lse, partial rounds
+  const double t_spread0 = 6.8516, t_spread_split = 0.2097;  // every split merges a share after a rendezvous
+  const double us_per_mb_part = 0.072;    // partial bytes written and read back (combine launch)
   const double mb = 1.0 / (1 << 20);
   const int grid = B * q_len * kHeadGroups * nsplit;
   const int rounds = (grid + cus - 1) / cus;
@@ -114,6 +116,8 @@ double est_time_us(int B, int q_len, int nsplit, int chunk_tiles, int cus, int m
   if (nsplit > 1) {
     if (merge == SMLA_MERGE_IN_KERNEL)
       t += t_fused0 + t_fused_split * nsplit;
+    else if (merge == SMLA_MERGE_SPREAD)
+      t += t_spread0 + t_spread_split * nsplit;
     else
       t += t_sep0 + t_sep_split * nsplit + us_per_mb_part * mb * 2.0 * B * q_len * nsplit * kHeads * kDv * 4.0;
   }
@@ -158,7 +162,7 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
     if (ov->tile_tokens != 0 && ov->tile_tokens != kTile) return SMLA_ERR_PLAN;
     if (ov->heads_per_wg != 0 && ov->heads_per_wg != kHpw) return SMLA_ERR_PLAN;
     if (ov->wg_per_cu < 0 || ov->wg_per_cu > 1) return SMLA_ERR_PLAN;
-    if (ov->merge < SMLA_MERGE_AUTO || ov->merge > SMLA_MERGE_SEPARATE) return SMLA_ERR_PLAN;
+    if (ov->merge < SMLA_MERGE_AUTO || ov->merge > SMLA_MERGE_SPREAD) return SMLA_ERR_PLAN;
     p.nsplit = ov->nsplit;
     p.merge = ov->merge;
   }
@@ -176,14 +180,18 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
     const int chunk = (kTiles + ns - 1) / ns;
     if ((kTiles + chunk - 1) / chunk != ns) continue;   // only split counts with no empty split
     if (forced != 0 && ns != forced) continue;
-    for (int m = SMLA_MERGE_IN_KERNEL; m <= SMLA_MERGE_SEPARATE; ++m) {
+    for (int m = SMLA_MERGE_IN_KERNEL; m <= SMLA_MERGE_SPREAD; ++m) {
       if (p.merge != SMLA_MERGE_AUTO && m != p.merge) continue;
-      if (m == SMLA_MERGE_IN_KERNEL && ns > 1 && query_sets(shape) > kMaxMergeSets) continue;
+      if ((m == SMLA_MERGE_IN_KERNEL || m == SMLA_MERGE_SPREAD) && ns > 1 && query_sets(shape) > kMaxMergeSets)
+        continue;
+      // the spread merge waits for every split of a request, so all of the
+      // launch's workgroups must be resident at once
+      if (m == SMLA_MERGE_SPREAD && ns > 1 && (int64_t)query_sets(shape) * kHeadGroups * ns > slots) continue;
       const double t = est_time_us(B > 0 ? B : 1, q_len_of(shape), ns, chunk, slots, m, smla_row_bytes(shape->kv_format));
       if (t < best - 1e-9) { best = t; best_ns = ns; best_merge = m; }
     }
   }
-  if (!std::isfinite(best)) return SMLA_ERR_PLAN;   // in-kernel merge forced beyond kMaxMergeSets
+  if (!std::isfinite(best)) return SMLA_ERR_PLAN;   // a forced merge placement this shape cannot take
   p.nsplit = best_ns;
   p.merge = p.nsplit > 1 ? best_merge : SMLA_MERGE_AUTO;
   *out = p;
@@ -277,6 +285,7 @@ static int prepare(const void* q, const void* kv_pool, const int32_t* page_table
   a.counters = nullptr;
   a.status = nullptr;
   a.spin_limit = merge_spin_limit();
+  a.spread = plan.merge == SMLA_MERGE_SPREAD ? 1 : 0;
   if (plan.nsplit > 1) {
     a.counters = (uint32_t*)workspace;
     a.status = (uint32_t*)((uint8_t*)workspace + kCountersOnly);
@@ -327,7 +336,8 @@ int smla::decode_with_workspace(const void* q, const void* kv_pool, const int32_
     if (launch_combine(pr.combine, pr.Q, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
     return SMLA_OK;
   }
-  // one launch: the last split of each request merges the partials
+  // one launch: the last split of each request merges the partials (or
+  // every split a share of them)
   if (launch_split(pr.split, pr.fmt, pr.Q * kHeadGroups * pr.nsplit, (hipStream_t)stream) != hipSuccess) return SMLA_ERR_HIP;
   // validate mode: wait, and report a merge that gave up (the workspace status word)
   if (pr.nsplit > 1 && validate_mode()) {

@@ -51,6 +51,7 @@ struct SplitArgs {
   uint32_t* counters;          // [qs][head group][2] tickets / finished writes; non-null: the last split merges
   uint32_t* status;            // workspace status word (non-zero: a merge gave up waiting; see sparse_mla.h)
   int spin_limit;              // polls before a merging workgroup gives up
+  int spread;                  // with counters: every split merges a share (all splits resident at once)
 };
 
 struct CombineArgs {

@@ -252,6 +252,10 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The spread merge: a (query set, head group) partial is 64 runs of 1 KB;
+// partials are loaded up to 8 splits at a time.
+constexpr int kRunsPerGroup = 4 * 4 * 4;
+constexpr int kSpreadBatch = 8;
 // Wait until every global store this wave issued has completed.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -399,6 +403,60 @@ __device__ __forceinline__ void merge_fused(const float* __restrict__ part_o, co
       uint16_t* orow = out + ((int64_t)b * kHeads + kHpw * hb + l32) * kDv + 128 * vb + 32 * (db0 + i) + 8 * j + 4 * kg;
       *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
     }
+}
+
+// The spread merge of (query set vr, head group hg): split `own` of nsplit
+// merges runs [64 own / nsplit, 64 (own + 1) / nsplit) of the group's 64
+// partial runs (8 dims x 32 heads each) once every split has written its
+// partial; the 12 waves take the share's runs in turn.  Same weights and the
+// same split-ordered accumulation as the combine kernel, so the bits agree.
+// Split 0 writes the merged lse.  A split whose wait gave up (`failed`) writes
+// NaN into its share of out and into the group's lse.
+__device__ __forceinline__ void merge_spread(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                             int nsplit, int vr, int hg, int own, bool failed,
+                                             uint16_t* __restrict__ out, float* __restrict__ lse, float* wt) {
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63, l32 = lane & 31, kg = lane >> 5;
+  const float* ls = part_lse + (int64_t)vr * nsplit * kHeads + kHpw * hg;
+  const int r0 = (kRunsPerGroup * own) / nsplit, r1 = (kRunsPerGroup * (own + 1)) / nsplit;
+  // first run of this wave: its loads go out with the lse loads
+  const int rw = r0 + wave;
+  f32x4 v[kSpreadBatch];
+  auto issue = [&](int r, int sp0) {
+    const int vb = r >> 4, db = (r >> 2) & 3, jj = r & 3;
+#pragma unroll
+    for (int u = 0; u < kSpreadBatch; ++u)
+      v[u] = r < r1 && sp0 + u < nsplit
+                 ? load_run(part_o, (int64_t)vr * nsplit + sp0 + u, part_run_offset(vb, db, jj, hg, lane))
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  issue(rw, 0);
+  const float lv = t < nsplit * kHpw ? load_agent(ls + (t >> 5) * kHeads + (t & (kHpw - 1))) : 0.f;
+  if (t < nsplit * kHpw) wt[t] = lv;
+  lds_barrier();
+  if (t < kHpw) {   // in place, column t
+    const float l = split_weights(nsplit, [&](int sp) { return wt[sp * kHpw + t]; }, wt + t, kHpw);
+    if (failed) lse[(int64_t)vr * kHeads + kHpw * hg + t] = __builtin_nanf("");
+    else if (own == 0) lse[(int64_t)vr * kHeads + kHpw * hg + t] = l;
+  }
+  lds_barrier();
+  for (int r = rw; r < r1; r += kWaves) {
+    if (r != rw) issue(r, 0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < nsplit; sp0 += kSpreadBatch) {
+      if (sp0 > 0) issue(r, sp0);
+#pragma unroll
+      for (int u = 0; u < kSpreadBatch; ++u) {
+        if (sp0 + u >= nsplit) break;
+        acc += wt[(sp0 + u) * kHpw + l32] * v[u];
+      }
+    }
+    const int vb = r >> 4, db = (r >> 2) & 3, jj = r & 3;
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    uint16_t* orow = out + ((int64_t)vr * kHeads + kHpw * hg + l32) * kDv + 128 * vb + 32 * db + 8 * jj + 4 * kg;
+    *reinterpret_cast<uint2*>(orow) = failed ? make_uint2(0x7fc07fc0u, 0x7fc07fc0u) : make_uint2(lo, hi);
+  }
 }
 
 // The row loads of one split on one loader wave: NT tiles, N 16-byte loads
@@ -854,8 +912,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // group) now, so its latency overlaps that tile.  The holder of the last
     // ticket merges.
     if (fused && threadIdx.x == 0) {
-      last_s = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(a.nsplit - 1);
+      last_s = !a.spread && __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                (uint32_t)(a.nsplit - 1);
       poison_s = __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
     }
     // this half's max and sum of each head for the PV waves
@@ -1059,6 +1117,35 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
     // no split can tell whether it is the last: lse is NaN (out is left as
     // is) until smla_workspace_init clears the workspace.
     if (threadIdx.x < kHpw) a.lse[(int64_t)vr * kHeads + kHpw * hg + threadIdx.x] = __builtin_nanf("");
+    return;
+  }
+  if (a.spread) {
+    // Every split merges a share once all have written: count this split's
+    // arrival, wait (bounded) for the others, then count it as done waiting.
+    // The split that finds every other done resets both counters: by then no
+    // split is still polling.  (All splits of the launch are resident at
+    // once: the host forms this plan only for grids of at most one
+    // workgroup per compute unit.)
+    wait_stores();
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool done = false;
+      for (int it = 0; it < a.spin_limit && !done; ++it) {
+        done = __hip_atomic_load(&ctr[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)a.nsplit;
+        if (!done) __builtin_amdgcn_s_sleep(2);
+      }
+      if (!done) __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(&ctr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          (uint32_t)(a.nsplit - 1)) {
+        __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      fail_s = done ? 0 : 1;
+    }
+    lds_barrier();
+    merge_spread(a.part_o, a.part_lse, a.nsplit, vr, hg, s, fail_s != 0, a.out, a.lse,
+                 reinterpret_cast<float*>(rowaddr_s));
     return;
   }
   if (!last_s) {

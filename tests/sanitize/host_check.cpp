@@ -102,6 +102,8 @@ hipError_t launch_split(const SplitArgs& a, int fmt, int nblocks, hipStream_t) {
   touch_read(a.topk_idx, (int64_t)g_ex.B * kTopk);
   touch_read(a.ctx_len, g_ex.B);
   const bool fused = a.nsplit > 1 && a.counters != nullptr;
+  CHECK(a.spread == 0 || a.spread == 1);
+  if (a.spread && fused) CHECK(nblocks <= 256);   // every split waits for the others: one resident round
   if (a.nsplit == 1 || fused) {
     touch_write(a.out, (int64_t)Q * kHeads * kDv);
     touch_write(a.lse, (int64_t)Q * kHeads);
@@ -279,13 +281,17 @@ void test_plans_and_decode() {
         if ((int64_t)B * (q_len ? q_len : 1) > 5000) continue;
         CHECK(decode_case(B, q_len, fmt, nullptr) == SMLA_OK);
         for (int ns = 1; ns <= 16; ++ns)
-          for (int m = SMLA_MERGE_AUTO; m <= SMLA_MERGE_SEPARATE; ++m) {
+          for (int m = SMLA_MERGE_AUTO; m <= SMLA_MERGE_SPREAD; ++m) {
             // the full grid up to B = 33; larger batches (partials of GBs) at
             // a few split counts and one query token
             if (B > 33 && (q_len > 1 || (ns > 4 && ns != 16) || (B > 96 && ns > 2))) continue;
             smla_plan pl = {ns, 0, 0, 0, m};
             const int rc = decode_case(B, q_len, fmt, &pl);
-            const bool over = m == SMLA_MERGE_IN_KERNEL && ns > 1 && B * (q_len ? q_len : 1) > 4096;
+            const int Q = B * (q_len ? q_len : 1);
+            const int chunk = (kTiles + ns - 1) / ns, ns_eff = (kTiles + chunk - 1) / chunk;
+            // the spread merge only for grids resident at once (256 CUs here)
+            const bool over = ns > 1 && (((m == SMLA_MERGE_IN_KERNEL || m == SMLA_MERGE_SPREAD) && Q > 4096) ||
+                                         (m == SMLA_MERGE_SPREAD && Q * kHeadGroups * ns_eff > 256));
             CHECK(rc == (over ? SMLA_ERR_PLAN : SMLA_OK));
             if (m == SMLA_MERGE_AUTO && ns > 1 && B > 0 && B <= 96) CHECK(decode_case(B, q_len, fmt, &pl, true) == SMLA_OK);
           }
@@ -370,7 +376,7 @@ void test_argument_errors() {
   CHECK(smla_plan_for_cus(&s, nullptr, 0, &p, &need) == SMLA_ERR_INVALID_ARG);
   CHECK(smla_plan_for_cus(&s, nullptr, 256, nullptr, &need) == SMLA_ERR_INVALID_ARG);
   for (smla_plan bp : {smla_plan{17, 0, 0, 0, 0}, smla_plan{-1, 0, 0, 0, 0}, smla_plan{0, 16, 0, 0, 0},
-                       smla_plan{0, 0, 64, 0, 0}, smla_plan{0, 0, 0, 2, 0}, smla_plan{0, 0, 0, 0, 3},
+                       smla_plan{0, 0, 64, 0, 0}, smla_plan{0, 0, 0, 2, 0}, smla_plan{0, 0, 0, 0, 4},
                        smla_plan{0, 0, 0, 0, -1}})
     CHECK(smla_plan_for_cus(&s, &bp, 256, &p, &need) == SMLA_ERR_PLAN);
   // every CU count gives a plan within bounds

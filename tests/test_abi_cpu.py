@@ -81,7 +81,7 @@ def test_null_pointers_and_bad_scale():
 def test_plan_overrides_validated():
     s = _shape()
     for bad in ({"nsplit": 17}, {"nsplit": -1}, {"tile_tokens": 16}, {"heads_per_wg": 64}, {"wg_per_cu": 3},
-                {"merge": 3}, {"merge": -1}):
+                {"merge": 4}, {"merge": -1}):
         with pytest.raises(smla.SmlaError) as e:
             smla.plan_for_cus(s, 256, bad)
         assert e.value.code == smla.ERR_PLAN
@@ -105,7 +105,9 @@ def test_selector_is_shape_only_and_bounded():
         p, ws = smla.plan_for_cus(_shape(batch=B), 256)
         assert 1 <= p.nsplit <= 16
         # a merge placement exactly when there is something to merge
-        assert (p.merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE)) == (p.nsplit > 1)
+        assert (p.merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE, smla.MERGE_SPREAD)) == (p.nsplit > 1)
+        if p.merge == smla.MERGE_SPREAD:   # only when the whole grid is resident at once
+            assert B * 2 * p.nsplit <= 256
         p2, ws2 = smla.plan_for_cus(_shape(batch=B), 256)
         assert p.as_dict() == p2.as_dict() and ws == ws2
     # with many requests the grid already fills the device: no split needed
@@ -153,7 +155,7 @@ def test_pages_worked_grid_numbers():
     assert sk["B"] * sk["H"] * sk["nsplit"] == sk["blocks"]
 
 
-@pytest.mark.parametrize("merge", [1, 2])
+@pytest.mark.parametrize("merge", [1, 2, 3])
 def test_forced_merge_placement_is_kept(merge):
     p, ws = smla.plan_for_cus(_shape(batch=8), 256, {"nsplit": 4, "merge": merge})
     assert (p.nsplit, p.merge) == (4, merge)
@@ -204,6 +206,26 @@ def test_in_kernel_merge_limited_to_counter_head():
         assert p.merge == smla.MERGE_SEPARATE
         with pytest.raises(smla.SmlaError):
             smla.plan_for_cus(_shape(batch=B, q_len=q), 256, {"nsplit": 2, "merge": smla.MERGE_IN_KERNEL})
+
+
+def test_spread_merge_needs_a_resident_grid():
+    """The spread merge has every split wait for its request's other splits, so
+    a plan takes it only while the whole grid (query sets x 2 head groups x
+    nsplit workgroups, one per compute unit) fits the device at once; forcing
+    it beyond that, or beyond the counter head's 4096 query sets, is refused."""
+    spread = smla.MERGE_SPREAD
+    p, ws = smla.plan_for_cus(_shape(batch=8), 256, {"nsplit": 16, "merge": spread})   # 256 workgroups
+    assert (p.nsplit, p.merge) == (16, spread) and ws > 0
+    for B, q, ns, cus in ((9, 1, 16, 256), (8, 1, 16, 255), (33, 1, 4, 256), (5, 4, 8, 256), (4097, 1, 2, 20000)):
+        with pytest.raises(smla.SmlaError) as e:
+            smla.plan_for_cus(_shape(batch=B, q_len=q), cus, {"nsplit": ns, "merge": spread})
+        assert e.value.code == smla.ERR_PLAN
+    # the automatic choice keeps to the same bound
+    for B in range(1, 129):
+        for q in (1, 2):
+            p, _ = smla.plan_for_cus(_shape(batch=B, q_len=q), 256)
+            if p.merge == spread:
+                assert B * q * 2 * p.nsplit <= 256, (B, q, p.as_dict())
 
 
 def test_read_rows_validation():

@@ -19,7 +19,8 @@ def _say(msg):
 
 
 @pytest.mark.parametrize("plan", [{"nsplit": 1}, {"nsplit": 4, "merge": smla.MERGE_IN_KERNEL},
-                                  {"nsplit": 3, "merge": smla.MERGE_SEPARATE}], ids=["ns1", "ns4_fused", "ns3_sep"])
+                                  {"nsplit": 3, "merge": smla.MERGE_SEPARATE}, {"nsplit": 8, "merge": smla.MERGE_SPREAD}],
+                         ids=["ns1", "ns4_fused", "ns3_sep", "ns8_spread"])
 def test_graph_replay_equals_eager(plan):
     """Every replay gives the eager bits, and the first replay of every layer
     matches the oracle (the layer loop of one decode step as one graph)."""

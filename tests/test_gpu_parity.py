@@ -84,7 +84,7 @@ def test_decode_b1_in_fp8_format():
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
 def test_decode_forced_nsplit(nsplit, fmt):
     w = W.build("nsplit", 930, fmt, 6, [65536, 4096, 700, 513, 300, 131072], fmt, "uniform")
-    for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+    for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE, smla.MERGE_SPREAD):
         _check(w, plan={"nsplit": nsplit, "merge": merge}, what=f"forced nsplit={nsplit} merge={merge} fmt={fmt}")
 
 
@@ -240,8 +240,9 @@ def test_empty_batch_and_errors():
 
 
 def test_split_and_combine_stages_equal_decode():
-    """In-kernel merge, separate-launch merge and the two stages called one by
-    one give identical bits (same weights, same split-ordered sums)."""
+    """In-kernel merge, separate-launch merge, the spread merge (where the grid
+    fits the device) and the two stages called one by one give identical bits
+    (same weights, same split-ordered sums)."""
     w = W.make(2)
     d = upload(w)
     shape = smla.make_shape(w.B, d.kv_format, d.page_table.shape[1], d.pool_pages)
@@ -249,7 +250,8 @@ def test_split_and_combine_stages_equal_decode():
         plan, ws_bytes = smla.plan_for(shape, ns)
         ws = smla.new_workspace(ws_bytes)
         res = []
-        for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+        merges = (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) + ((smla.MERGE_SPREAD,) if ns in (3, 4) else ())
+        for merge in merges:
             o = torch.empty((w.B, 64, 512), dtype=torch.bfloat16, device="cuda")
             l = torch.empty((w.B, 64), dtype=torch.float32, device="cuda")
             pl = {"nsplit": ns, "merge": merge}
@@ -283,6 +285,23 @@ def test_fused_merge_repeated_calls_share_workspace():
         assert_parity(out, lse, ref_o, ref_l, f"fused merge call {it} {w.name} nsplit={ns}")
 
 
+def test_spread_merge_repeated_calls_share_workspace():
+    """The spread merge and the last-split merge take turns on one workspace,
+    across plans and batch sizes: each call leaves its counters at zero."""
+    ws = smla.new_workspace(80 << 20)
+    spread, fused = smla.MERGE_SPREAD, smla.MERGE_IN_KERNEL
+    for it, (wid, ns, merge) in enumerate([(2, 4, spread), (2, 4, spread), (2, 4, fused), (1, 16, spread),
+                                           (2, 3, spread), (1, 8, fused), (1, 8, spread), (2, 4, spread)]):
+        w = W.make(wid)
+        pool = w.host_pool()
+        d = upload(w)
+        out, lse = smla.decode(d.q, d.pool, d.page_table, d.topk_idx, d.ctx_len, d.scale, kv_format=d.kv_format,
+                               pool_pages=d.pool_pages, plan={"nsplit": ns, "merge": merge}, workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.decode_workload(w, pool=pool)
+        assert_parity(out, lse, ref_o, ref_l, f"merge {merge} call {it} {w.name} nsplit={ns}")
+
+
 def test_workspace_init_recovers_dirty_counters():
     w = W.make(2)
     d = upload(w)
@@ -308,7 +327,8 @@ def test_query_tokens_share_selection(q_len):
     w = _mtp_workload(q_len)
     _check(w, what=f"q_len={q_len} auto plan")
     for ns in (1, 2, 5):
-        for merge in ((smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE) if ns > 1 else (smla.MERGE_AUTO,)):
+        merges = (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE, smla.MERGE_SPREAD) if ns > 1 else (smla.MERGE_AUTO,)
+        for merge in merges:
             _check(w, plan={"nsplit": ns, "merge": merge}, what=f"q_len={q_len} nsplit={ns} merge={merge}")
 
 
@@ -416,17 +436,16 @@ def test_dominant_late_token_rescales_live_accumulators(fmt):
     w = _dominant_workload(fmt)
     ref_o, ref_l = oracle.decode_workload(w)
     assert ref_l.min() > 20.0, ref_l.min()          # the planted token dominates every head
-    for ns in (1, 16):
-        _check(w, plan={"nsplit": ns, "merge": smla.MERGE_IN_KERNEL if ns > 1 else smla.MERGE_AUTO},
-               what=f"dominant late token nsplit={ns} fmt={fmt}")
+    for ns, merge in ((1, smla.MERGE_AUTO), (16, smla.MERGE_IN_KERNEL), (16, smla.MERGE_SPREAD)):
+        _check(w, plan={"nsplit": ns, "merge": merge}, what=f"dominant late token nsplit={ns} merge={merge} fmt={fmt}")
 
 
 @pytest.mark.parametrize("fmt", [W.FMT_FP8, W.FMT_BF16])
 def test_merge_of_splits_with_far_apart_lse(fmt):
     """The dominant token sits in one split, so that split's lse is ~25 nats above
-    the others' and their weights underflow to ~1e-11: both merge placements and
-    the two-stage form must give the oracle's result (and each other's bits)."""
+    the others' and their weights underflow to ~1e-11: every merge placement must
+    give the oracle's result."""
     w = _dominant_workload(fmt)
     for ns in (2, 4, 16):
-        for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE):
+        for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE, smla.MERGE_SPREAD):
             _check(w, plan={"nsplit": ns, "merge": merge}, what=f"far-apart lse nsplit={ns} merge={merge} fmt={fmt}")
