@@ -834,10 +834,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
         p[i] = v;
         tmax = fmaxf(tmax, v);
       }
-      tmax = wave_max16(tmax);
       float m_cur = m_run;
       float alpha = 1.0f;
+      // the head's max over its 16 tokens passes m_cur + 8 exactly when one of
+      // its four lanes' own maxima does: reduce across lanes only then
       if (__builtin_amdgcn_ballot_w64(tmax > m_cur + 8.0f)) {
+        tmax = wave_max16(tmax);
         const float m_new = (tmax > m_cur + 8.0f) ? tmax : m_cur;
         alpha = __builtin_amdgcn_exp2f(m_cur - m_new);   // 0 when nothing was seen before
         m_cur = m_new;
