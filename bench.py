@@ -300,7 +300,10 @@ def main() -> int:
     # decomposition that reads each row once.  (d) reads the rows of every
     # input set in one launch over all compute units (16 layers' worth, no
     # launch or ramp in the way): the sustained rate of this random gather;
-    # (e) the same number of rows, consecutive in the pool, for comparison.
+    # (e) the same number of rows, consecutive in the pool, for comparison;
+    # (f) the decode's layout over rows that all sit in L2 (512 random rows
+    # per group drawn from 2000): what one compute unit's memory path moves
+    # when no row waits for HBM.
     row_read = None
     if not args.no_row_read:
         t3 = time.time()
@@ -318,7 +321,8 @@ def main() -> int:
         order = torch.tensor(order, dtype=torch.long, device=dev)
         valid_rows = float(np.mean([int((sl >= 0).sum()) for sl in slot_sets]))
         row_read = {}
-        for name in ("decode_layout", "request_once", "each_row_once", "all_sets_once", "all_sets_consecutive"):
+        for name in ("decode_layout", "request_once", "each_row_once", "all_sets_once", "all_sets_consecutive",
+                     "l2_resident"):
             if name == "decode_layout":
                 lists = [sl[order].reshape(-1).contiguous() for sl in slot_sets]
                 per, groups, n_rows = 512, 2 * B, 2 * valid_rows
@@ -333,11 +337,15 @@ def main() -> int:
                 lists = [torch.cat([sl.reshape(-1) for sl in slot_sets]).contiguous()]
                 per = -(-lists[0].numel() // n_cu)
                 groups, n_rows = -(-lists[0].numel() // per), valid_rows * len(slot_sets)
-            else:
+            elif name == "all_sets_consecutive":
                 n_all = sum(sl.numel() for sl in slot_sets)
                 lists = [torch.arange(n_all, dtype=torch.long, device=dev)]
                 per = -(-n_all // n_cu)
                 groups, n_rows = -(-n_all // per), n_all
+            else:
+                gen = torch.Generator().manual_seed(7)
+                lists = [torch.randint(0, 2000, (2 * B * 512,), generator=gen).to(dev) for _ in range(8)]
+                per, groups, n_rows = 512, 2 * B, 2 * B * 512
             sink = torch.empty(groups * 1024, dtype=torch.int32, device=dev)
 
             def read(lst, per=per, groups=groups, sink=sink):
