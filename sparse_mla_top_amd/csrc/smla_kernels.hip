@@ -6,7 +6,9 @@
 //                    against Q as fp8 hi + lo; bf16 MFMA for the rope and for
 //                    bf16 rows), online softmax, PV on bf16 MFMA, and write a
 //                    normalised partial (O, lse) -- or the final output when the
-//                    request is not split; optionally the last split merges.
+//                    request is not split; optionally the splits merge in the
+//                    same launch (the last split to finish, or every split a
+//                    share once all have written).
 //   combine kernel : log-sum-exp merge of the partials of each (request, head).
 //   gather kernel  : the translation + gather stage alone (test hook).
 //
@@ -543,7 +545,8 @@ __device__ __forceinline__ void load_rows_nt(const uint64_t LDS_AS* rowaddr_s, u
 //     32g..32g+31, so the products pair the same dims.
 //     Online softmax in the log2 domain per head (lane column) and half; the
 //     running max is only raised when a tile's max exceeds it by more than
-//     2^8, so the output is rarely rescaled (p stays <= 2^8).  P^T goes to LDS,
+//     2^8, so the output is rarely rescaled (p stays <= 2^8), and the tile's
+//     max is reduced across lanes only when some lane's own scores do.  P^T goes to LDS,
 //     one bf16 copy per scale block with that block's scales folded in.
 //   PV waves 4..7 own latent dims 128v..128v+127 (scale block v = w-4) for
 //     the group's 32 heads: O^T[32 d][32 heads] += V^T[32 d][16 tok] .
