@@ -112,7 +112,8 @@ typedef struct {
 #define SMLA_MERGE_SPREAD 3    /* the same launch: once every split of a request has written
                                   its partial, each merges an equal share of the dims; only
                                   when every workgroup of the launch is resident at once
-                                  (batch * q_len * 2 * nsplit <= compute units) and for
+                                  (batch * q_len * 2 * nsplit <= compute units; the selector
+                                  picks it itself only up to half of them) and for
                                   batch * q_len <= 4096 (a plan forcing it otherwise returns
                                   SMLA_ERR_PLAN)                                           */
 

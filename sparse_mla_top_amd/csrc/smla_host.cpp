@@ -185,8 +185,12 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* ov, int num_cus,
       if ((m == SMLA_MERGE_IN_KERNEL || m == SMLA_MERGE_SPREAD) && ns > 1 && query_sets(shape) > kMaxMergeSets)
         continue;
       // the spread merge waits for every split of a request, so all of the
-      // launch's workgroups must be resident at once
-      if (m == SMLA_MERGE_SPREAD && ns > 1 && (int64_t)query_sets(shape) * kHeadGroups * ns > slots) continue;
+      // launch's workgroups must be resident at once; chosen automatically
+      // only while the grid leaves half the CUs free (a margin for CUs that
+      // other work on the device may hold), forced up to every CU
+      if (m == SMLA_MERGE_SPREAD && ns > 1 &&
+          (int64_t)query_sets(shape) * kHeadGroups * ns > (p.merge == SMLA_MERGE_SPREAD ? slots : slots / 2))
+        continue;
       const double t = est_time_us(B > 0 ? B : 1, q_len_of(shape), ns, chunk, slots, m, smla_row_bytes(shape->kv_format));
       if (t < best - 1e-9) { best = t; best_ns = ns; best_merge = m; }
     }
