@@ -134,7 +134,7 @@ int smla_row_bytes(int kv_format) {
   return -1;
 }
 
-int smla_version(void) { return 102; }
+int smla_version(void) { return 103; }
 
 const char* smla_strerror(int code) {
   switch (code) {
