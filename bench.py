@@ -362,8 +362,35 @@ def main() -> int:
                               "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                               "frac_of_device_copy": round(gbs / copy_gbs, 4)}
         del slot_sets
+        # The launch floor: smla_read_rows over one skipped row on as many
+        # workgroups as the device has CUs (nothing read but the slot), back
+        # to back on the stream and as 42 launches replayed as one graph.
+        one = torch.full((1,), -1, dtype=torch.long, device=dev)
+        fsink = torch.empty(n_cu * 1024, dtype=torch.int32, device=dev)
+
+        def empty_launch(st=None):
+            rc = smla.read_rows_raw(pool, pool_pages * W.PAGE, one, 1, w0.row_bytes, n_cu, fsink, st or stream)
+            if rc != 0:
+                raise RuntimeError(f"read_rows failed: {smla.strerror(rc)}")
+        warm(empty_launch, 256, 0.05)
+        eager_us = repeat_stats([timed(empty_launch, 1000) for _ in range(3)])["median_us"]
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        fgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            empty_launch(gs)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(fgraph, stream=gs):
+                for _ in range(LAYERS_PER_STEP):
+                    empty_launch(gs)
+        torch.cuda.synchronize()
+        warm(fgraph.replay, 20, 0.05)
+        graph_us = repeat_stats([timed(fgraph.replay, 50) for _ in range(3)])["median_us"] / LAYERS_PER_STEP
+        del fgraph
+        row_read["launch_floor"] = {"workgroups": n_cu, "eager_us": eager_us, "graph_us": round(graph_us, 3)}
         log(f"row reads alone done in {time.time() - t3:.1f}s: "
-            f"{ {k: (v['us'], v['GBps'], v['groups']) for k, v in row_read.items()} }")
+            f"{ {k: (v['us'], v['GBps'], v['groups']) for k, v in row_read.items() if 'us' in v} } "
+            f"launch floor {row_read['launch_floor']}")
 
     # ------------------------------------------------------------------ query tokens
     # q_len query tokens per request sharing its selection, on the headline
