@@ -170,8 +170,8 @@ int smla_plan_for_cus(const smla_shape* shape, const smla_plan* override_or_null
  *   workspace  [device] scratch of at least the size smla_plan_for reports
  *                        (may be NULL when that size is 0).  Its first 64 KiB +
  *                        256 B hold the arrival counters of the merges in the
- *                        same launch and a status word, at the same place for every shape and
- *                        plan; the split partials follow.  It must be zero-filled
+ *                        same launch and a status word, at the same place for
+ *                        every shape and plan; the split partials follow.  It must be zero-filled
  *                        once before its first use (smla_workspace_init); every
  *                        successful call leaves the counters at zero again, so one
  *                        workspace serves calls of any batch size and split count
