@@ -220,12 +220,13 @@ def test_spread_merge_needs_a_resident_grid():
         with pytest.raises(smla.SmlaError) as e:
             smla.plan_for_cus(_shape(batch=B, q_len=q), cus, {"nsplit": ns, "merge": spread})
         assert e.value.code == smla.ERR_PLAN
-    # the automatic choice keeps the grid within half the device
-    for B in range(1, 129):
-        for q in (1, 2):
-            p, _ = smla.plan_for_cus(_shape(batch=B, q_len=q), 256)
-            if p.merge == spread:
-                assert B * q * 2 * p.nsplit <= 128, (B, q, p.as_dict())
+    # the automatic choice keeps the grid within half the device, whatever its size
+    for cus in (32, 120, 256, 304):
+        for B in range(1, 129, 3):
+            for q in (1, 2):
+                p, _ = smla.plan_for_cus(_shape(batch=B, q_len=q), cus)
+                if p.merge == spread:
+                    assert B * q * 2 * p.nsplit <= cus // 2, (cus, B, q, p.as_dict())
 
 
 def test_read_rows_validation():
