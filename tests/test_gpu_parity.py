@@ -130,6 +130,9 @@ def test_masked_and_degenerate_requests():
     w = W.build("degenerate", 940, 0, 6, [1000, 8, 512, 5000, 50, 3000], W.FMT_FP8, "given", topk_idx=idx)
     for ns in (1, 4, 16):
         _check(w, plan=ns, what=f"degenerate nsplit={ns}")
+    # splits that hold no valid slot at all (lse -inf) under every merge placement
+    for merge in (smla.MERGE_IN_KERNEL, smla.MERGE_SEPARATE, smla.MERGE_SPREAD):
+        _check(w, plan={"nsplit": 16, "merge": merge}, what=f"degenerate nsplit=16 merge={merge}")
 
 
 def test_q_zero_and_single_token_closed_forms():
