@@ -1081,15 +1081,25 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) res[db] = o[db][0] * f[0] + o[db][1] * f[1];
     if (a.nsplit == 1) {
-      uint16_t* orow = a.out + ((int64_t)vr * kHeads + ghead) * kDv + 128 * vb + 4 * kg;
+      // this wave's 32 heads x 128 dims go through LDS (the ring is free now),
+      // so each store writes 1 KB of whole rows: 4 heads x 256 bytes
+      constexpr int kStRow = 128 * 2 + 16;   // bytes per head row, padded off the bank period
+      uint8_t* stg = smem + vb * (kHpw * kStRow);
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const uint32_t lo = (uint32_t)f32_to_bf16_rne(res[db][4 * jj]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 1]) << 16);
           const uint32_t hi = (uint32_t)f32_to_bf16_rne(res[db][4 * jj + 2]) | ((uint32_t)f32_to_bf16_rne(res[db][4 * jj + 3]) << 16);
-          *reinterpret_cast<uint2*>(orow + 32 * db + 8 * jj) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(stg + l32 * kStRow + 2 * (32 * db + 8 * jj + 4 * kg)) = make_uint2(lo, hi);
         }
+      uint16_t* obase = a.out + ((int64_t)vr * kHeads + kHpw * hg) * kDv + 128 * vb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = lane + 64 * i, h = c >> 4, pc = c & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + h * kStRow + 16 * pc);
+        *reinterpret_cast<uint4*>(obase + (int64_t)h * kDv + 8 * pc) = v;
+      }
     } else if (!fused || !last_s) {
       const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)vr * a.nsplit + s) * (kHeads * kDv), kPartBytes);
 #pragma unroll
