@@ -491,7 +491,8 @@ __device__ __forceinline__ void load_rows(const uint64_t LDS_AS* rowaddr_s, uint
       const int slot = (int)(dst[q] >> 4);
       const int row = slot / TL::kChunksRow, chunk = slot - row * TL::kChunksRow;
       const uint64_t src = (rowaddr_s[t * kTile + row] & ~1ull) + 16 * chunk;
-      d[q] = *reinterpret_cast<const u32x4 GLOBAL_AS*>(static_cast<uintptr_t>(src));
+      // non-temporal: each row passes through this CU once (B=80: 0.3-0.5 us faster than plain loads)
+      d[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 GLOBAL_AS*>(static_cast<uintptr_t>(src)));
     }
   };
   auto write = [&](int t, const u32x4 (&d)[N]) {
@@ -1097,8 +1098,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(SplitArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = lane + 64 * i, h = c >> 4, pc = c & 15;
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + h * kStRow + 16 * pc);
-        *reinterpret_cast<uint4*>(obase + (int64_t)h * kDv + 8 * pc) = v;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + h * kStRow + 16 * pc);
+        // non-temporal: nothing in this launch reads the output back
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)h * kDv + 8 * pc));
       }
     } else if (!fused || !last_s) {
       const __amdgpu_buffer_rsrc_t r = buffer_of(a.part_o + ((int64_t)vr * a.nsplit + s) * (kHeads * kDv), kPartBytes);
