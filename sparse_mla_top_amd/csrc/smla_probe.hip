@@ -55,9 +55,10 @@ __global__ __launch_bounds__(kProbeThreads) void read_rows_kernel(const uint8_t*
   uint32_t keep[kProbeDepth], knext[kProbeDepth];
   const u32x4* next[kProbeDepth];
 #pragma unroll
-  for (int d = 0; d < kProbeDepth; ++d) v[d] = *piece(d, keep[d]);
+  for (int d = 0; d < kProbeDepth; ++d) v[d] = __builtin_nontemporal_load(piece(d, keep[d]));
 #pragma unroll
   for (int d = 0; d < kProbeDepth; ++d) next[d] = piece(kProbeDepth + d, knext[d]);
+  // loads carry the non-temporal hint, as the decode's row loads do.
   // each step consumes the oldest load and issues the next into its slot; the
   // addresses of the following round are computed (LDS reads) while the
   // round's loads are in flight
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_rows_kernel(const uint8_t*
 #pragma unroll
     for (int d = 0; d < kProbeDepth; ++d) {
       acc ^= v[d] & keep[d];
-      v[d] = *next[d];
+      v[d] = __builtin_nontemporal_load(next[d]);
       keep[d] = knext[d];
       __builtin_amdgcn_sched_barrier(0);
     }
